@@ -1,0 +1,139 @@
+"""Seeded synthetic inputs for triangular attention.
+
+This module is shared by the FP64 oracle tests, the GPU parity tests and the
+benchmark.  It only draws random numbers and rounds them to bf16; it holds none
+of the attention arithmetic.
+
+Shapes follow the TurboPairFormer notation table (Table 1): Q, K, V, O and the
+incoming gradient dO are ``[B, N_o, H, N, D]`` (N_o outer slices of N x D per
+head), the pair bias shared by every slice is ``[B, H, N, N]`` indexed
+``[query, key]`` (Figure 6, step 3), and the optional per-slice key mask is an
+additive ``[B, N_o, N]`` FP32 tensor (0 keeps a key, -1e9 masks it).
+
+Draw order for one seed is fixed: Q, K, V, dO, bias, then the mask uniforms.
+All draws happen in FP32 on the CPU with ``torch.Generator``; inputs whose
+dtype is bf16 are rounded once with round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+MASK_VALUE = -1.0e9
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    N_o: int
+    N: int
+    H: int
+    D: int
+    scale: float
+    bias_std: float = 1.0
+    mask_p: float = 0.0          # Bernoulli probability that a key is masked
+    bf16: bool = True            # round Q/K/V/dO/bias to bf16
+    description: str = ""
+
+    @property
+    def flops_fwd_bwd(self) -> float:
+        """FlashAttention-style count: 4 (QK^T, PV) + 10 (S recompute, dV, dP, dQ, dK) x D per score."""
+        return 14.0 * self.B * self.N_o * self.H * self.N * self.N * self.D
+
+    @property
+    def flops_fwd(self) -> float:
+        return 4.0 * self.B * self.N_o * self.H * self.N * self.N * self.D
+
+    @property
+    def flops_bwd(self) -> float:
+        return 10.0 * self.B * self.N_o * self.H * self.N * self.N * self.D
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+def _w(name, N, H, D, scale, **kw):
+    return Workload(name=name, B=1, N_o=N, N=N, H=H, D=D, scale=scale, **kw)
+
+
+#: The workloads the method is measured on (crop sizes 384/640/768, head dims 16/32, H=4).
+WORKLOADS = {
+    "tiny": _w("tiny", 32, 2, 16, 0.25, bf16=False,
+               description="B=1 N_o=N=32 H=2 D=16, fp32 N(0,1) inputs and bias, scale 1/4, no mask"),
+    "n384_d32": _w("n384_d32", 384, 4, 32, 1.0 / math.sqrt(32),
+                   description="B=1 N_o=N=384 H=4 D=32 bf16 N(0,1), bias N(0,1), scale 1/sqrt(32), no mask"),
+    "n640_d16": _w("n640_d16", 640, 4, 16, 0.25, bias_std=2.0,
+                   description="B=1 N_o=N=640 H=4 D=16 bf16 N(0,1), bias N(0, std 2), scale 1/4, no mask"),
+    "n768_d32_mask": _w("n768_d32_mask", 768, 4, 32, 1.0 / math.sqrt(32), mask_p=0.1,
+                        description="B=1 N_o=N=768 H=4 D=32 bf16 N(0,1), bias N(0,1), "
+                                    "per-slice key mask Bernoulli(0.1) additive -1e9, scale 1/sqrt(32)"),
+}
+
+#: The six-shape sweep: crops {384, 640, 768} x head dims {16, 32}, H=4, no mask.
+SWEEP = {f"sweep_n{n}_d{d}": _w(f"sweep_n{n}_d{d}", n, 4, d, 1.0 / math.sqrt(d),
+                                description=f"B=1 N_o=N={n} H=4 D={d} bf16 N(0,1), bias N(0,1), "
+                                            f"scale 1/sqrt({d}), no mask")
+         for n in (384, 640, 768) for d in (16, 32)}
+
+
+def get(name: str) -> Workload:
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    if name in SWEEP:
+        return SWEEP[name]
+    raise KeyError(name)
+
+
+def make_inputs(w: Workload, seed: int, bf16: Optional[bool] = None) -> dict:
+    """Draw the inputs of one fwd+bwd call.
+
+    Returns CPU tensors: ``q, k, v, do`` ``[B,N_o,H,N,D]`` and ``bias`` ``[B,H,N,N]``
+    as float32 (holding bf16-representable values when rounding is on), plus
+    ``mask`` ``[B,N_o,N]`` float32 or ``None``.
+    """
+    round_bf16 = w.bf16 if bf16 is None else bf16
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    shp = (w.B, w.N_o, w.H, w.N, w.D)
+    q = torch.randn(shp, generator=g, dtype=torch.float32)
+    k = torch.randn(shp, generator=g, dtype=torch.float32)
+    v = torch.randn(shp, generator=g, dtype=torch.float32)
+    do = torch.randn(shp, generator=g, dtype=torch.float32)
+    bias = torch.randn((w.B, w.H, w.N, w.N), generator=g, dtype=torch.float32) * w.bias_std
+    mask = None
+    if w.mask_p > 0.0:
+        u = torch.rand((w.B, w.N_o, w.N), generator=g, dtype=torch.float32)
+        keep = u >= w.mask_p
+        # every slice keeps at least one key (a fully masked slice has no
+        # well-defined softmax); at p=0.1 and N>=32 a failure has odds < 1e-32
+        assert bool(keep.any(dim=-1).all()), "a slice has every key masked"
+        mask = torch.where(keep, torch.zeros((), dtype=torch.float32),
+                           torch.full((), MASK_VALUE, dtype=torch.float32))
+    out = {"q": q, "k": k, "v": v, "do": do, "bias": bias}
+    if round_bf16:
+        out = {n: t.to(torch.bfloat16).to(torch.float32) for n, t in out.items()}
+    out["mask"] = mask
+    return out
+
+
+def random_mask(B: int, N_o: int, N: int, p: float, seed: int) -> torch.Tensor:
+    """Additive key mask [B,N_o,N] with P(masked)=p; every slice keeps key 0..N-1 at least once."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    u = torch.rand((B, N_o, N), generator=g, dtype=torch.float32)
+    keep = u >= p
+    none_kept = ~keep.any(dim=-1)
+    keep[..., 0] |= none_kept
+    return torch.where(keep, torch.zeros((), dtype=torch.float32),
+                       torch.full((), MASK_VALUE, dtype=torch.float32))
+
+
+def bf16_tensor(shape, seed: int, std: float = 1.0) -> torch.Tensor:
+    """A seeded N(0, std) tensor rounded to bf16 (returned as float32)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return (torch.randn(shape, generator=g, dtype=torch.float32) * std).to(torch.bfloat16).to(torch.float32)
