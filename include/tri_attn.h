@@ -1,0 +1,140 @@
+/*
+ * tri_attn.h -- C ABI of the MI355X (gfx950) triangular-attention library.
+ *
+ * Operation: triangular attention with a pair bias shared by every outer slice,
+ * as defined in "TurboPairFormer: Fast and Stable Protein Folding Model
+ * Training with an Optimized Triangle Attention Kernel" (notation table,
+ * Table 1; Figure 1(a); worked example, Figure 6).  For example b, outer slice
+ * o and head h, with N x D matrices Q, K, V taken from the pairs (o, .):
+ *
+ *   s[q,k]  = scale * <Q[q], K[k]> + bias[b,h,q,k] + mask[b,o,k]
+ *   P[q,:]  = softmax_k(s[q,:]),  O[q] = sum_k P[q,k] V[k]
+ *
+ * The bias is the same for every o; scale multiplies the dot product only.
+ * The backward produces dQ, dK, dV and dbias = sum_o dS_o (three reduction
+ * axes: keys, queries, outer slices; Figure 1(a)).
+ *
+ * Data layout (all tensors dense, row-major, no strides):
+ *   Q, K, V, O, E, dO, dQ, dK, dV  [B, N_o, H, N, D]   bf16 (bit patterns)
+ *   bias, dbias                    [B, H, N, N]        bf16, indexed [query, key]
+ *   mask                           [B, N_o, N]         fp32 additive (0 keeps a key,
+ *                                                      -1e9 removes it), or NULL
+ *   lse, delta                     [B, N_o, H, N]      fp32 (lse in natural log)
+ *   dq_partial                     [J_K, B, N_o, H, N, D] fp32
+ *   dbias_partial                  [L,   B, H, N, N]      fp32
+ * with J_K = ceil(N / key tile) and L = ceil(N_o / outer group) as reported by
+ * tri_attn_workspace().
+ *
+ * Ownership: every pointer is a DEVICE pointer owned by the caller.  The
+ * library allocates nothing, frees nothing and never synchronises; each call
+ * only enqueues kernels on `stream` and returns.  Inputs may alias each other
+ * read-only; outputs must not alias any other argument.  The library holds no
+ * mutable global state, so calls on distinct buffers may run concurrently.
+ *
+ * Errors: arguments are checked on the host before any launch.  A null
+ * required pointer gives TRI_ATTN_ERR_NULL, a bad dimension or scale
+ * TRI_ATTN_ERR_SHAPE, an unsupported head dimension TRI_ATTN_ERR_UNSUPPORTED,
+ * a pointer not 16-byte aligned TRI_ATTN_ERR_ALIGN, and a failed launch
+ * TRI_ATTN_ERR_LAUNCH; in every error case nothing has been enqueued except
+ * for TRI_ATTN_ERR_LAUNCH.  Device faults surface at the caller's next
+ * synchronisation, as for any HIP call.  NaN and Inf inputs propagate.
+ *
+ * Determinism: for fixed dimensions and build, every output is bitwise
+ * reproducible across calls on the same GPU model.  No float atomics are
+ * used; every sum has a fixed order.
+ */
+#ifndef TRI_ATTN_H
+#define TRI_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TRI_ATTN_OK = 0,
+  TRI_ATTN_ERR_NULL = 1,
+  TRI_ATTN_ERR_SHAPE = 2,
+  TRI_ATTN_ERR_UNSUPPORTED = 3,
+  TRI_ATTN_ERR_ALIGN = 4,
+  TRI_ATTN_ERR_LAUNCH = 5
+} tri_attn_status;
+
+/* Problem dimensions.  D must be 16 or 32; B, N_o, H, N >= 1; scale finite. */
+typedef struct {
+  int64_t B, N_o, H, N, D;
+  float scale;
+} tri_attn_dims;
+
+typedef uint16_t tri_bf16; /* bfloat16 bit pattern */
+
+/* Opaque HIP stream (hipStream_t); NULL is the default stream. */
+typedef void* tri_attn_stream;
+
+/*
+ * Forward (Figure 6 steps 1-4; online softmax over key tiles).
+ * Writes O = bf16(O32) with O32 the FP32 normalised output, the output
+ * residual E = bf16(O32 - O) when o_res is not NULL (the saved BF16
+ * approximation of the output-rounding residual: Abstract, Figure 7(b)), and
+ * lse = max_k s + log(sum_k exp(s - max)) per row.  O is bitwise the same
+ * whether or not o_res is given.
+ */
+tri_attn_status tri_attn_fwd(const tri_attn_dims* d,
+                             const tri_bf16* q, const tri_bf16* k, const tri_bf16* v,
+                             const tri_bf16* bias, const float* mask /* may be NULL */,
+                             tri_bf16* o, tri_bf16* o_res /* may be NULL */, float* lse,
+                             tri_attn_stream stream);
+
+/*
+ * Softmax correction (Figure 7(b)): delta[row] = sum_d dO[row,d] * (O[row,d] + E[row,d])
+ * in FP32 with a fixed order; with o_res == NULL it is sum_d dO * O (no compensation).
+ */
+tri_attn_status tri_attn_bwd_delta(const tri_attn_dims* d, const tri_bf16* o,
+                                   const tri_bf16* o_res /* may be NULL */,
+                                   const tri_bf16* d_o, float* delta,
+                                   tri_attn_stream stream);
+
+/*
+ * Main key-tile backward (Figure 2, Figure 7(c)).  One workgroup owns one key
+ * tile of one head for one outer group of slices and visits every query tile,
+ * evaluating S, P, dP and dS once.  dK and dV (scaled by `scale` for dK) are
+ * finished in the workgroup; dQ (already scaled) leaves as one FP32 partial per
+ * key tile and dbias as one FP32 partial per outer group, each element written
+ * by exactly one workgroup (Figure 11(a), materialised partials).
+ */
+tri_attn_status tri_attn_bwd(const tri_attn_dims* d,
+                             const tri_bf16* q, const tri_bf16* k, const tri_bf16* v,
+                             const tri_bf16* bias, const float* mask /* may be NULL */,
+                             const tri_bf16* d_o, const float* lse, const float* delta,
+                             tri_bf16* dk, tri_bf16* dv,
+                             float* dq_partial, float* dbias_partial,
+                             tri_attn_stream stream);
+
+/* dQ = bf16(sum_{t=0..J_K-1} dq_partial[t]), summed in ascending t in FP32 (Figure 7(d)). */
+tri_attn_status tri_attn_reduce_dq(const tri_attn_dims* d, const float* dq_partial,
+                                   tri_bf16* dq, tri_attn_stream stream);
+
+/* dbias = bf16(sum_{l=0..L-1} dbias_partial[l]), summed in ascending l in FP32 (Figure 7(d)). */
+tri_attn_status tri_attn_reduce_dbias(const tri_attn_dims* d, const float* dbias_partial,
+                                      tri_bf16* dbias, tri_attn_stream stream);
+
+/*
+ * Partial-buffer sizes for these dimensions (elements, FP32), the number of
+ * key tiles J_K and of outer groups L, and the key-tile / group sizes used.
+ * Any output pointer may be NULL.  Host-only arithmetic; no device access.
+ */
+tri_attn_status tri_attn_workspace(const tri_attn_dims* d, int64_t* dq_partial_elems,
+                                   int64_t* dbias_partial_elems, int64_t* j_k, int64_t* l,
+                                   int64_t* key_tile, int64_t* outer_group);
+
+/* Human-readable name of a status code (static string). */
+const char* tri_attn_status_string(tri_attn_status s);
+
+/* Library version, e.g. "0.1.0". */
+const char* tri_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TRI_ATTN_H */

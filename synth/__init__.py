@@ -137,3 +137,24 @@ def bf16_tensor(shape, seed: int, std: float = 1.0) -> torch.Tensor:
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
     return (torch.randn(shape, generator=g, dtype=torch.float32) * std).to(torch.bfloat16).to(torch.float32)
+
+
+def make_inputs_device(w: Workload, seed: int, device="cuda") -> dict:
+    """Seeded inputs drawn on the device (for tests that need many large inputs and no
+    oracle): same shapes, distributions and bf16 rounding as ``make_inputs``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    shp = (w.B, w.N_o, w.H, w.N, w.D)
+    out = {}
+    for n in ("q", "k", "v", "do"):
+        out[n] = torch.randn(shp, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    out["bias"] = (torch.randn((w.B, w.H, w.N, w.N), generator=g, device=device, dtype=torch.float32)
+                   * w.bias_std).to(torch.bfloat16)
+    out["mask"] = None
+    if w.mask_p > 0.0:
+        u = torch.rand((w.B, w.N_o, w.N), generator=g, device=device, dtype=torch.float32)
+        keep = u >= w.mask_p
+        keep[..., 0] |= ~keep.any(dim=-1)
+        out["mask"] = torch.where(keep, torch.zeros((), device=device),
+                                  torch.full((), MASK_VALUE, device=device)).float()
+    return out

@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol the header declares, validates its arguments before touching the device,
+and sizes its partial buffers as the memory table of the method prescribes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from triangular_attention_amd import _lib
+    return _lib.load()
+
+
+def _header_symbols():
+    txt = open(os.path.join(ROOT, "include", "tri_attn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(tri_attn_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from triangular_attention_amd import _lib
+    syms = _header_symbols()
+    assert set(syms) == set(_lib.EXPORTS)
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert lib.tri_attn_version().decode().count(".") == 2
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.tri_attn_status_string(code)
+    assert lib.tri_attn_status_string(99) == b"unknown status"
+
+
+def _dims(**kw):
+    from triangular_attention_amd import _lib
+    base = dict(B=1, N_o=8, H=2, N=8, D=32, scale=0.125)
+    base.update(kw)
+    return _lib.Dims(base["B"], base["N_o"], base["H"], base["N"], base["D"], base["scale"])
+
+
+P = ctypes.c_void_p(0x100000)       # aligned, never dereferenced on the host
+MIS = ctypes.c_void_p(0x100008)     # 8-byte aligned only
+
+
+def _fwd(lib, d, **ptrs):
+    a = dict(q=P, k=P, v=P, bias=P, mask=None, o=P, o_res=None, lse=P)
+    a.update(ptrs)
+    return lib.tri_attn_fwd(None if d is None else ctypes.byref(d), a["q"], a["k"], a["v"], a["bias"],
+                            a["mask"], a["o"], a["o_res"], a["lse"], None)
+
+
+def test_validation_errors_before_launch(lib):
+    assert _fwd(lib, None) == 1
+    assert _fwd(lib, _dims(D=64)) == 3
+    assert _fwd(lib, _dims(D=8)) == 3
+    assert _fwd(lib, _dims(N=0)) == 2
+    assert _fwd(lib, _dims(B=0)) == 2
+    assert _fwd(lib, _dims(scale=float("nan"))) == 2
+    assert _fwd(lib, _dims(scale=float("inf"))) == 2
+    assert _fwd(lib, _dims(), q=None) == 1
+    assert _fwd(lib, _dims(), lse=None) == 1
+    assert _fwd(lib, _dims(), k=MIS) == 4
+    assert _fwd(lib, _dims(), mask=MIS) == 4
+    assert _fwd(lib, _dims(), o_res=MIS) == 4
+    d = _dims()
+    assert lib.tri_attn_bwd_delta(ctypes.byref(d), P, None, None, P, None) == 1
+    assert lib.tri_attn_bwd_delta(ctypes.byref(d), P, MIS, P, P, None) == 4
+    assert lib.tri_attn_bwd(ctypes.byref(d), P, P, P, P, None, P, P, P, P, P, P, None, None) == 1
+    assert lib.tri_attn_bwd(ctypes.byref(d), P, P, P, P, None, P, P, P, P, P, MIS, P, None) == 4
+    assert lib.tri_attn_bwd(ctypes.byref(_dims(D=48)), P, P, P, P, None, P, P, P, P, P, P, P, None) == 3
+    assert lib.tri_attn_reduce_dq(ctypes.byref(d), None, P, None) == 1
+    assert lib.tri_attn_reduce_dq(ctypes.byref(d), P, MIS, None) == 4
+    assert lib.tri_attn_reduce_dbias(ctypes.byref(d), P, None, None) == 1
+    assert lib.tri_attn_reduce_dbias(ctypes.byref(_dims(H=0)), P, P, None) == 2
+
+
+def test_python_binding_raises(lib):
+    from triangular_attention_amd import _lib
+    with pytest.raises(_lib.TriAttnError):
+        _lib.check("tri_attn_fwd", _fwd(lib, _dims(D=64)))
+
+
+def _golden_table2():
+    rows = []
+    for line in open(os.path.join(ROOT, "tests", "golden", "table2_alloc_mib.txt")):
+        if line.strip() and not line.startswith("#"):
+            rows.append([int(x) for x in line.split()])
+    return rows
+
+
+def test_workspace_matches_memory_table():
+    """Partial sizes follow the memory table (Table 2) with the same tiles (key tile 64,
+    outer group 4); ours are FP32, so twice the table's BF16 bytes."""
+    from triangular_attention_amd import api
+    mib = float(2 ** 20)
+    for N, WQ, Wb_all, Wb_res, WE, WdS in _golden_table2():
+        d = _dims(B=1, N_o=N, H=4, N=N, D=32)
+        ws = api.workspace(d)
+        assert ws["key_tile"] == 64 and ws["outer_group"] == 4
+        assert ws["j_k"] == N // 64 and ws["l"] == N // 4
+        assert ws["dq_partial_elems"] * 2 / mib == WQ            # BF16 bytes of the same count
+        assert ws["dbias_partial_elems"] * 2 / mib == Wb_all
+        assert ws["dq_partial_elems"] * 4 / mib == 2 * WQ         # what we actually allocate
+        assert N * 4 * N * 32 * 2 / mib == WE                     # residual E, one bf16 Q-sized tensor
+        assert N * 4 * N * N * 4 / mib == WdS                     # dense dS, never stored
+        assert Wb_res <= Wb_all
+
+
+def test_workspace_ragged():
+    from triangular_attention_amd import api
+    ws = api.workspace(_dims(B=2, N_o=10, H=3, N=65, D=16))
+    assert ws["j_k"] == 2 and ws["l"] == 3
+    assert ws["dq_partial_elems"] == 2 * 2 * 10 * 3 * 65 * 16
+    assert ws["dbias_partial_elems"] == 3 * 2 * 3 * 65 * 65

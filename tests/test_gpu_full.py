@@ -1,0 +1,125 @@
+"""GPU checks at the full workload sizes (crops 384/640/768, D 16/32, H=4):
+
+* parity on sampled outputs the oracle computes one by one (whole slices for
+  O, dQ, dK, dV; whole rows of dbias, which sum over every slice);
+* bitwise replay: five calls give identical dQ, dK, dV, dbias (and O), with
+  every output and partial buffer poisoned with NaN before each call
+  (TurboPairFormer, Figure 10 protocol);
+* the residual-compensation ablation: O and dV bitwise equal with and without
+  the residual, and the dQ, dK and dbias errors smaller with it (Figure 9).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import np64, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL_O, TOL_G = 5e-3, 1.5e-2
+FULL = ["n384_d32", "n640_d16", "n768_d32_mask"]
+
+
+def _poisoned_call(ta, dev, scale, compensate=True):
+    q = dev["q"]
+    B, N_o, H, N, D = q.shape
+    d = ta.dims_of(q, scale)
+    ws = ta.workspace(d)
+    nan = float("nan")
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    o = torch.full(q.shape, nan, **bf)
+    o_res = torch.full(q.shape, nan, **bf) if compensate else None
+    lse = torch.full((B, N_o, H, N), nan, device="cuda")
+    delta = torch.full((B, N_o, H, N), nan, device="cuda")
+    dk, dv, dq = (torch.full(q.shape, nan, **bf) for _ in range(3))
+    dbias = torch.full((B, H, N, N), nan, **bf)
+    dqp = torch.full((ws["dq_partial_elems"],), nan, device="cuda")
+    dbp = torch.full((ws["dbias_partial_elems"],), nan, device="cuda")
+    ta.tri_attn_fwd(d, q, dev["k"], dev["v"], dev["bias"], dev["mask"], o, o_res, lse)
+    ta.tri_attn_bwd_delta(d, o, o_res, dev["do"], delta)
+    ta.tri_attn_bwd(d, q, dev["k"], dev["v"], dev["bias"], dev["mask"], dev["do"], lse, delta, dk, dv, dqp, dbp)
+    ta.tri_attn_reduce_dq(d, dqp, dq)
+    ta.tri_attn_reduce_dbias(d, dbp, dbias)
+    torch.cuda.synchronize()
+    return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "dbias": dbias}
+
+
+def _samples(w, x, got, n_slices=3, n_rows=6, seed=0):
+    rng = np.random.default_rng(seed)
+    slices = [(0, 0), (0, w.N_o - 1)] + [(0, int(o)) for o in rng.choice(np.arange(1, w.N_o - 1), n_slices - 2,
+                                                                            replace=False)]
+    rows = [(0, int(rng.integers(w.H)), int(rng.integers(w.N))) for _ in range(n_rows)]
+    ref_s = oracle.backward_slices(x["q"], x["k"], x["v"], x["bias"], x["mask"], w.scale, x["do"], slices)
+    ref_r = oracle.dbias_rows(x["q"], x["k"], x["v"], x["bias"], x["mask"], w.scale, x["do"], rows)
+    err = {}
+    for n in ("o", "dq", "dk", "dv"):
+        g = np.stack([np64(got[n][b, o]) for (b, o) in slices])
+        err[n] = oracle.rel_rmse(g, ref_s[n])
+    g = np.stack([np64(got["dbias"][b, h, i]) for (b, h, i) in rows])
+    err["dbias"] = oracle.rel_rmse(g, ref_r)
+    g = np.stack([np64(got["lse"][b, o]) for (b, o) in slices])
+    err["lse_abs"] = float(np.max(np.abs(g - ref_s["lse"])))
+    return err
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(name):
+    ta = require_gpu()
+    w = synth.get(name)
+    print(f"full-size parity {name}", flush=True)
+    x = synth.make_inputs(w, 0)
+    got = _poisoned_call(ta, to_dev(x), w.scale)
+    err = _samples(w, x, got)
+    print(name, err, flush=True)
+    assert err["o"] <= TOL_O, err
+    for n in ("dq", "dk", "dv", "dbias"):
+        assert err[n] <= TOL_G, (n, err)
+    assert err["lse_abs"] <= 1e-3, err
+    for n in ("o", "dq", "dk", "dv", "dbias"):
+        assert torch.isfinite(got[n].float()).all(), n
+
+
+SHAPES = [(n, d) for n in (384, 640, 768) for d in (16, 32)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"n{s[0]}_d{s[1]}")
+def test_bitwise_replay(shape):
+    """Five calls per input, several seeded inputs per shape: every gradient bitwise identical."""
+    ta = require_gpu()
+    N, D = shape
+    w = synth.get(f"sweep_n{N}_d{D}")
+    seeds = range(1000, 1004)
+    for seed in seeds:
+        print(f"replay n{N} d{D} seed {seed}", flush=True)
+        ww = w.with_(mask_p=0.1) if seed % 2 else w
+        dev = synth.make_inputs_device(ww, seed)
+        first = _poisoned_call(ta, dev, w.scale)
+        for n in ("dq", "dk", "dv", "dbias", "o"):
+            assert torch.isfinite(first[n].float()).all(), (n, seed)
+        for _ in range(4):
+            again = _poisoned_call(ta, dev, w.scale)
+            for n in ("dq", "dk", "dv", "dbias", "o", "lse"):
+                assert torch.equal(again[n].view(torch.int16) if again[n].dtype == torch.bfloat16 else
+                                   again[n].view(torch.int32),
+                                   first[n].view(torch.int16) if first[n].dtype == torch.bfloat16 else
+                                   first[n].view(torch.int32)), (n, seed)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_residual_compensation_ablation(name):
+    ta = require_gpu()
+    w = synth.get(name)
+    print(f"ablation {name}", flush=True)
+    x = synth.make_inputs(w, 1)
+    dev = to_dev(x)
+    on = _poisoned_call(ta, dev, w.scale, compensate=True)
+    off = _poisoned_call(ta, dev, w.scale, compensate=False)
+    assert torch.equal(on["o"].view(torch.int16), off["o"].view(torch.int16))
+    assert torch.equal(on["dv"].view(torch.int16), off["dv"].view(torch.int16))
+    e_on = _samples(w, x, on, n_slices=6, n_rows=24, seed=5)
+    e_off = _samples(w, x, off, n_slices=6, n_rows=24, seed=5)
+    print(name, "with residual", e_on, "without", e_off, flush=True)
+    for n in ("dq", "dk", "dbias"):
+        assert e_on[n] < e_off[n], (n, e_on[n], e_off[n])

@@ -1,0 +1,97 @@
+"""ctypes binding of ``libtri_attn.so`` (the C ABI declared in include/tri_attn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  Loading fails loudly when the library has not been
+built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtri_attn.so")
+
+STATUS = {
+    0: "TRI_ATTN_OK",
+    1: "TRI_ATTN_ERR_NULL",
+    2: "TRI_ATTN_ERR_SHAPE",
+    3: "TRI_ATTN_ERR_UNSUPPORTED",
+    4: "TRI_ATTN_ERR_ALIGN",
+    5: "TRI_ATTN_ERR_LAUNCH",
+}
+
+#: every symbol include/tri_attn.h declares
+EXPORTS = (
+    "tri_attn_fwd",
+    "tri_attn_bwd_delta",
+    "tri_attn_bwd",
+    "tri_attn_reduce_dq",
+    "tri_attn_reduce_dbias",
+    "tri_attn_workspace",
+    "tri_attn_status_string",
+    "tri_attn_version",
+)
+
+
+class Dims(ctypes.Structure):
+    """Mirror of ``tri_attn_dims``."""
+    _fields_ = [
+        ("B", ctypes.c_int64),
+        ("N_o", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("D", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class TriAttnError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} returned {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (once).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m triangular_attention_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)
+    dp = ctypes.POINTER(Dims)
+    sig = {
+        "tri_attn_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "tri_attn_bwd_delta": [dp, vp, vp, vp, vp, vp],
+        "tri_attn_bwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "tri_attn_reduce_dq": [dp, vp, vp, vp],
+        "tri_attn_reduce_dbias": [dp, vp, vp, vp],
+        "tri_attn_workspace": [dp, i64p, i64p, i64p, i64p, i64p, i64p],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.tri_attn_status_string.argtypes = [ctypes.c_int]
+    lib.tri_attn_status_string.restype = ctypes.c_char_p
+    lib.tri_attn_version.argtypes = []
+    lib.tri_attn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def check(fn: str, code: int) -> None:
+    if code != 0:
+        msg = load().tri_attn_status_string(code).decode()
+        raise TriAttnError(fn, code, msg)
+
+
+def dims(B: int, N_o: int, H: int, N: int, D: int, scale: float) -> Dims:
+    return Dims(int(B), int(N_o), int(H), int(N), int(D), float(scale))

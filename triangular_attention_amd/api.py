@@ -1,0 +1,196 @@
+"""Python entry points with the names of the C ABI, plus an autograd function.
+
+The five calls (``tri_attn_fwd``, ``tri_attn_bwd_delta``, ``tri_attn_bwd``,
+``tri_attn_reduce_dq``, ``tri_attn_reduce_dbias``) take device tensors,
+check dtype/shape/contiguity, and pass raw pointers and the current HIP
+stream to the library.  PyTorch only supplies memory and the stream.
+
+``triangular_attention`` chains them as a ``torch.autograd.Function``:
+forward = ``tri_attn_fwd``; backward = delta -> main backward -> the two
+fixed-order reductions (TurboPairFormer, Figure 7(b)-(d)).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+MASK_VALUE = -1.0e9
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def dims_of(q: torch.Tensor, scale: float) -> _lib.Dims:
+    if q.dim() != 5:
+        raise ValueError("q must be [B, N_o, H, N, D]")
+    B, N_o, H, N, D = q.shape
+    return _lib.dims(B, N_o, H, N, D, scale)
+
+
+def workspace(d: _lib.Dims) -> dict:
+    """Partial-buffer sizes (``tri_attn_workspace``); host-only, no device access."""
+    lib = _lib.load()
+    vals = [ctypes.c_int64() for _ in range(6)]
+    _lib.check("tri_attn_workspace", lib.tri_attn_workspace(ctypes.byref(d), *[ctypes.byref(v) for v in vals]))
+    keys = ("dq_partial_elems", "dbias_partial_elems", "j_k", "l", "key_tile", "outer_group")
+    return {k: v.value for k, v in zip(keys, vals)}
+
+
+def tri_attn_fwd(d, q, k, v, bias, mask, o, o_res, lse, stream=None):
+    B, N_o, H, N, D = d.B, d.N_o, d.H, d.N, d.D
+    x = (B, N_o, H, N, D)
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _need(t, n, torch.bfloat16, x)
+    _need(bias, "bias", torch.bfloat16, (B, H, N, N))
+    if mask is not None:
+        _need(mask, "mask", torch.float32, (B, N_o, N))
+    if o_res is not None:
+        _need(o_res, "o_res", torch.bfloat16, x)
+    _need(lse, "lse", torch.float32, (B, N_o, H, N))
+    lib = _lib.load()
+    _lib.check("tri_attn_fwd", lib.tri_attn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+                                                _ptr(mask), _ptr(o), _ptr(o_res), _ptr(lse), _stream(stream)))
+
+
+def tri_attn_bwd_delta(d, o, o_res, d_o, delta, stream=None):
+    x = (d.B, d.N_o, d.H, d.N, d.D)
+    _need(o, "o", torch.bfloat16, x)
+    _need(d_o, "d_o", torch.bfloat16, x)
+    if o_res is not None:
+        _need(o_res, "o_res", torch.bfloat16, x)
+    _need(delta, "delta", torch.float32, (d.B, d.N_o, d.H, d.N))
+    lib = _lib.load()
+    _lib.check("tri_attn_bwd_delta", lib.tri_attn_bwd_delta(ctypes.byref(d), _ptr(o), _ptr(o_res), _ptr(d_o),
+                                                            _ptr(delta), _stream(stream)))
+
+
+def tri_attn_bwd(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv, dq_partial, dbias_partial, stream=None):
+    B, N_o, H, N, D = d.B, d.N_o, d.H, d.N, d.D
+    x = (B, N_o, H, N, D)
+    for n, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o), ("dk", dk), ("dv", dv)):
+        _need(t, n, torch.bfloat16, x)
+    _need(bias, "bias", torch.bfloat16, (B, H, N, N))
+    if mask is not None:
+        _need(mask, "mask", torch.float32, (B, N_o, N))
+    _need(lse, "lse", torch.float32, (B, N_o, H, N))
+    _need(delta, "delta", torch.float32, (B, N_o, H, N))
+    ws = workspace(d)
+    if dq_partial.dtype != torch.float32 or dq_partial.numel() < ws["dq_partial_elems"] or not dq_partial.is_contiguous():
+        raise ValueError(f"dq_partial must be contiguous float32 with >= {ws['dq_partial_elems']} elements")
+    if dbias_partial.dtype != torch.float32 or dbias_partial.numel() < ws["dbias_partial_elems"] or not dbias_partial.is_contiguous():
+        raise ValueError(f"dbias_partial must be contiguous float32 with >= {ws['dbias_partial_elems']} elements")
+    lib = _lib.load()
+    _lib.check("tri_attn_bwd", lib.tri_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
+                                                _ptr(d_o), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
+                                                _ptr(dq_partial), _ptr(dbias_partial), _stream(stream)))
+
+
+def tri_attn_reduce_dq(d, dq_partial, dq, stream=None):
+    _need(dq, "dq", torch.bfloat16, (d.B, d.N_o, d.H, d.N, d.D))
+    ws = workspace(d)
+    if dq_partial.dtype != torch.float32 or dq_partial.numel() < ws["dq_partial_elems"] or not dq_partial.is_contiguous():
+        raise ValueError("dq_partial has the wrong dtype or size")
+    lib = _lib.load()
+    _lib.check("tri_attn_reduce_dq", lib.tri_attn_reduce_dq(ctypes.byref(d), _ptr(dq_partial), _ptr(dq), _stream(stream)))
+
+
+def tri_attn_reduce_dbias(d, dbias_partial, dbias, stream=None):
+    _need(dbias, "dbias", torch.bfloat16, (d.B, d.H, d.N, d.N))
+    ws = workspace(d)
+    if dbias_partial.dtype != torch.float32 or dbias_partial.numel() < ws["dbias_partial_elems"] or not dbias_partial.is_contiguous():
+        raise ValueError("dbias_partial has the wrong dtype or size")
+    lib = _lib.load()
+    _lib.check("tri_attn_reduce_dbias", lib.tri_attn_reduce_dbias(ctypes.byref(d), _ptr(dbias_partial), _ptr(dbias),
+                                                                  _stream(stream)))
+
+
+# --------------------------------------------------------------------------- composite calls
+
+
+def forward(q, k, v, bias, mask=None, scale=None, compensate=True):
+    """Returns ``(o, o_res or None, lse)``."""
+    d = dims_of(q, (1.0 / math.sqrt(q.shape[-1])) if scale is None else scale)
+    o = torch.empty_like(q)
+    o_res = torch.empty_like(q) if compensate else None
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    tri_attn_fwd(d, q, k, v, bias, mask, o, o_res, lse)
+    return o, o_res, lse
+
+
+def backward(q, k, v, bias, mask, scale, o, o_res, lse, d_o, workspace_buffers=None):
+    """Delta, key-tile backward and the two reductions.  Returns ``(dq, dk, dv, dbias)``."""
+    d = dims_of(q, scale)
+    ws = workspace(d)
+    delta = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    tri_attn_bwd_delta(d, o, o_res, d_o, delta)
+    if workspace_buffers is None:
+        dq_part = torch.empty(ws["dq_partial_elems"], dtype=torch.float32, device=q.device)
+        db_part = torch.empty(ws["dbias_partial_elems"], dtype=torch.float32, device=q.device)
+    else:
+        dq_part, db_part = workspace_buffers
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    tri_attn_bwd(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv, dq_part, db_part)
+    dq = torch.empty_like(q)
+    dbias = torch.empty_like(bias)
+    tri_attn_reduce_dq(d, dq_part, dq)
+    tri_attn_reduce_dbias(d, db_part, dbias)
+    return dq, dk, dv, dbias
+
+
+class _TriAttn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, bias, mask, scale, compensate):
+        o, o_res, lse = forward(q, k, v, bias, mask, scale, compensate)
+        ctx.save_for_backward(q, k, v, bias, mask, o, o_res, lse)
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, d_o):
+        q, k, v, bias, mask, o, o_res, lse = ctx.saved_tensors
+        dq, dk, dv, dbias = backward(q, k, v, bias, mask, ctx.scale, o, o_res, lse, d_o.contiguous())
+        return dq, dk, dv, dbias, None, None, None
+
+
+def triangular_attention(q, k, v, bias, mask=None, scale=None, compensate=True):
+    """Triangular attention with a pair bias shared by every outer slice.
+
+    q, k, v: ``[B, N_o, H, N, D]`` bf16 (D in {16, 32}); bias ``[B, H, N, N]`` bf16;
+    mask: ``[B, N_o, N]`` additive float32, or a bool tensor (True = keep), or None.
+    Returns O ``[B, N_o, H, N, D]`` bf16; differentiable in q, k, v and bias.
+    """
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if mask is not None and mask.dtype == torch.bool:
+        mask = torch.where(mask, torch.zeros((), device=mask.device),
+                           torch.full((), MASK_VALUE, device=mask.device)).float()
+    if mask is not None:
+        mask = mask.contiguous()
+    return _TriAttn.apply(q.contiguous(), k.contiguous(), v.contiguous(), bias.contiguous(), mask,
+                          float(scale), bool(compensate))

@@ -1,0 +1,84 @@
+// Shared device helpers for the gfx950 triangular-attention kernels.
+//
+// MFMA operand convention used by every kernel (v_mfma_f32_16x16x32_bf16 and
+// v_mfma_f32_16x16x16_bf16): lane l = 16*g + c (g = lane group 0..3, c = 0..15).
+//   A operand: lane (g, c) supplies row c of A and the contraction slots of group g.
+//   B operand: lane (g, c) supplies column c of B and the slots of group g.
+//   Result:    lane (g, c) holds rows 4g+0..3 of column c.
+// The product sums A-slot (g, j) against B-slot (g, j) over all (g, j), so the
+// kernels are free to assign any contraction index to a slot as long as A and
+// B agree.  A 16x16 result block in bf16 therefore serves directly as the B
+// operand (or, transposed, as the A operand) of a product that contracts over
+// the block's rows: slots (g, 0..3) of one block and (g, 4..7) of a second.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tri {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Two floats -> two bf16 (round to nearest even, hardware v_cvt_pk_bf16_f32); a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint16_t f_to_bf(float a) { return (uint16_t)(pack_bf16(a, 0.f) & 0xffffu); }
+
+__device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// Contraction over the head dimension D (16 or 32) of one 16x16 block.
+// For D = 32 each lane supplies 8 values (slots d = 8g..8g+7), for D = 16 four (d = 4g..4g+3).
+template <int D> struct DOp;
+template <> struct DOp<32> {
+  typedef u32x4 T;
+  static constexpr int kPerLane = 8;
+  __device__ static __forceinline__ f32x4 mma(T a, T b, f32x4 c) { return mfma_k32(a, b, c); }
+};
+template <> struct DOp<16> {
+  typedef u32x2 T;
+  static constexpr int kPerLane = 4;
+  __device__ static __forceinline__ f32x4 mma(T a, T b, f32x4 c) { return mfma_k16(a, b, c); }
+};
+
+template <typename T> __device__ __forceinline__ T ld_shared(const uint16_t* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+template <typename T> __device__ __forceinline__ T ld_global(const void* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+
+__device__ __forceinline__ float wave_max_groups(float x) {
+  // max over the 4 lane groups that share a column (lanes c, c+16, c+32, c+48)
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_groups(float x) {
+  // fixed order: every lane ends with (x0 + x1) + (x2 + x3), commutative adds only
+  x = x + __shfl_xor(x, 16);
+  x = x + __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace tri

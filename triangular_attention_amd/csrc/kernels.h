@@ -1,0 +1,67 @@
+// Argument blocks and launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tri {
+
+// Tile constants of the key-tile backward.  J_K = ceil(N / kBwdKeyTile) dQ
+// partials and L = ceil(N_o / kBwdGroup) dbias partials.
+constexpr int kBwdKeyTile = 64;
+constexpr int kBwdGroup = 4;
+constexpr int kBwdQueryTile = 64;
+constexpr int kFwdQueryTile = 128;
+constexpr int kFwdKeyTile = 64;
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* bias;
+  const float* mask;
+  uint16_t* o;
+  uint16_t* o_res;
+  float* lse;
+  int B, N_o, H, N;
+  float scale;
+};
+
+struct DeltaArgs {
+  const uint16_t* o;
+  const uint16_t* o_res;
+  const uint16_t* d_o;
+  float* delta;
+  int64_t rows;
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* bias;
+  const float* mask;
+  const uint16_t* d_o;
+  const float* lse;
+  const float* delta;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dq_partial;
+  float* dbias_partial;
+  int B, N_o, H, N;
+  int n_key_tiles, n_groups;
+  float scale;
+};
+
+struct ReduceArgs {
+  const float* partial;
+  uint16_t* out;
+  int64_t elems;    // elements of one partial (== elements of the output)
+  int n_partials;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, int D, hipStream_t s);
+hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
+
+}  // namespace tri
