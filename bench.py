@@ -1,0 +1,238 @@
+"""Benchmark: triangular attention forward + backward on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input: tri_attn_fwd,
+tri_attn_bwd_delta, tri_attn_bwd, tri_attn_reduce_dq, tri_attn_reduce_dbias.
+Inputs, outputs and partial buffers are resident in HBM before timing starts.
+
+Prints ONE JSON line (rank 0) with the throughput in TFLOP/s (FlashAttention
+count 14*B*N_o*H*N^2*D per fwd+bwd), the per-kernel breakdown, the roofline
+of the dominant kernel (HIP events on the launch stream), and the FP64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published 2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published 8 TB/s)
+KERNELS = ("fwd", "delta", "bwd", "reduce_dq", "reduce_dbias")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="n768_d32_mask")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-compensate", action="store_true", help="run without the output residual")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch (from rocprofv3 counters), if present")
+    return ap.parse_args()
+
+
+def algorithmic(w, jk, L):
+    """Algorithmic flops and minimum HBM bytes of one launch of each kernel."""
+    X = w.B * w.N_o * w.H * w.N * w.D
+    Y = w.B * w.H * w.N * w.N
+    R = w.B * w.N_o * w.H * w.N
+    M = w.B * w.N_o * w.N if w.mask_p > 0 else 0
+    S = w.B * w.N_o * w.H * w.N * w.N
+    return {
+        "fwd": {"flops": 4.0 * S * w.D, "bytes": 2 * (3 * X + Y + 2 * X) + 4 * (M + R)},
+        "delta": {"flops": 2.0 * X, "bytes": 2 * 3 * X + 4 * R},
+        "bwd": {"flops": 10.0 * S * w.D,
+                "bytes": 2 * (4 * X + Y + 2 * X) + 4 * (2 * R + M) + 4 * (jk * X + L * Y)},
+        "reduce_dq": {"flops": float(jk * X), "bytes": 4 * jk * X + 2 * X},
+        "reduce_dbias": {"flops": float(L * Y), "bytes": 4 * L * Y + 2 * Y},
+    }
+
+
+def cpu_baseline(w, seconds):
+    """The FP64 oracle (as it stands) on the first S outer slices of the same workload."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    x = synth.make_inputs(w, 0)
+    sub = lambda t, s: None if t is None else t[:, :s].contiguous()
+
+    def run(s):
+        t0 = time.perf_counter()
+        oracle.backward(sub(x["q"], s), sub(x["k"], s), sub(x["v"], s), x["bias"], sub(x["mask"], s),
+                        w.scale, sub(x["do"], s))
+        return time.perf_counter() - t0
+
+    s0 = min(4, w.N_o)
+    t0 = run(s0)
+    s = int(max(s0, min(w.N_o, s0 * seconds / max(t0, 1e-3))))
+    t = run(s) if s != s0 else t0
+    flops = 14.0 * w.B * s * w.H * w.N * w.N * w.D
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fwd+bwd of outer slices 0..{s - 1} of {w.N_o} (all heads, all queries/keys) "
+                      f"of workload {w.name}, seed 0, FP64 numpy; {t:.1f} s",
+            "seconds": t, "slices": s, "threads_note": "BLAS threads (numpy elementwise ops run on one core)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described in DESIGN.md but not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import triangular_attention_amd as ta
+
+    ta.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.get(args.workload)
+    x = synth.make_inputs(w, args.seed)
+    q, k, v, do, bias = (x[n].to(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do", "bias"))
+    mask = None if x["mask"] is None else x["mask"].to(dev)
+    d = ta.dims_of(q, w.scale)
+    ws = ta.workspace(d)
+    comp = not args.no_compensate
+    o = torch.empty_like(q)
+    o_res = torch.empty_like(q) if comp else None
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dk, dv, dq = torch.empty_like(k), torch.empty_like(v), torch.empty_like(q)
+    dbias = torch.empty_like(bias)
+    dqp = torch.empty(ws["dq_partial_elems"], dtype=torch.float32, device=dev)
+    dbp = torch.empty(ws["dbias_partial_elems"], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    calls = {
+        "fwd": lambda: ta.tri_attn_fwd(d, q, k, v, bias, mask, o, o_res, lse, stream),
+        "delta": lambda: ta.tri_attn_bwd_delta(d, o, o_res, do, delta, stream),
+        "bwd": lambda: ta.tri_attn_bwd(d, q, k, v, bias, mask, do, lse, delta, dk, dv, dqp, dbp, stream),
+        "reduce_dq": lambda: ta.tri_attn_reduce_dq(d, dqp, dq, stream),
+        "reduce_dbias": lambda: ta.tri_attn_reduce_dbias(d, dbp, dbias, stream),
+    }
+
+    def step():
+        for n in KERNELS:
+            calls[n]()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+
+    # per-kernel durations: events on the launch stream around each kernel, K more steps
+    per = {n: 0.0 for n in KERNELS}
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        evs[s][0].record(stream)
+        for i, n in enumerate(KERNELS):
+            calls[n]()
+            evs[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        for i, n in enumerate(KERNELS):
+            per[n] += evs[s][i].elapsed_time(evs[s][i + 1]) / args.steps
+
+    alg = algorithmic(w, ws["j_k"], ws["l"])
+    kernels = {}
+    for n in KERNELS:
+        ms = per[n]
+        kernels[n] = {"ms": round(ms, 5),
+                      "tflops": round(alg[n]["flops"] / (ms * 1e-3) / 1e12, 2) if ms > 0 else None,
+                      "alg_gbs": round(alg[n]["bytes"] / (ms * 1e-3) / 1e9, 1) if ms > 0 else None}
+    dom = max(KERNELS, key=lambda n: per[n])
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            tr = json.load(open(args.traffic))
+            entry = tr.get(w.name, {}).get(dom)
+            if entry and entry.get("kernel_hash") == kernel_hash():
+                traffic = entry.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    if dom in ("bwd", "fwd"):
+        ach = alg[dom]["flops"] / (per[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "avg_launch_ms": round(per[dom], 5)}
+    else:
+        ach = alg[dom]["bytes"] / (per[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "avg_launch_ms": round(per[dom], 5)}
+
+    value = w.flops_fwd_bwd / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": "tri-attn fwd+bwd TFLOP/s & ms at N=768,H=4,D=32 bf16; % bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N_o": w.N_o, "N": w.N, "H": w.H, "D": w.D,
+                   "scale": w.scale, "bias_std": w.bias_std, "mask_p": w.mask_p,
+                   "compensate": comp, "flops_per_step": w.flops_fwd_bwd,
+                   "key_tile": ws["key_tile"], "outer_group": ws["outer_group"],
+                   "description": w.description},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels": kernels,
+        "roofline": roof,
+        "wall_s_timed": round(t_wall, 4),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+def kernel_hash():
+    """Hash of the kernel sources: stored traffic counters are valid only for the same code."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "triangular_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

