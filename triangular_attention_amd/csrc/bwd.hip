@@ -12,62 +12,77 @@
 //
 // Orientation: S = Q K^T with queries as MFMA rows and keys as columns; each
 // wave owns 16 keys.  In this layout the bf16 P and dS blocks are directly the
-// operands of dV^T = dO^T P and dK^T = Q^T dS (contraction over queries), so
-// only dS needs to be re-laid out (through LDS) for dQ^T = K^T dS^T.  The
-// per-query softmax statistics (lse, delta) are per-register values; -delta
-// is folded into the accumulator input of the dP product.
+// B operands of dV^T = dO^T P and dK^T = Q^T dS (contraction over queries);
+// the dO^T and Q^T operands come from the row-major LDS tiles through the
+// transposing LDS read.  dS is stored key-major in LDS and read back, also
+// transposed, as the operand of dQ^T = K^T dS^T.  -lse/scale and -delta enter
+// as the accumulator inputs of the S and dP products, so the exponent costs
+// one FMA per score.  Q/dO tiles are double-buffered: one barrier per
+// (query tile, slice) stage.
 #include "common.h"
 #include "kernels.h"
 
 namespace tri {
 
-template <int D, bool MASK, bool VEC>
-__global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
-  constexpr int TK = kBwdKeyTile, TQ = kBwdQueryTile, G = kBwdGroup;
-  constexpr int QP = D + 8;     // row-major Q / dO tile pitch
-  constexpr int TP = TQ + 8;    // transposed Q^T / dO^T tile pitch
-  constexpr int SP = TK + 8;    // dS tile pitch (row = query)
-  constexpr int KTP = TK + 8;   // K^T tile pitch (row = feature)
-  constexpr int CH = D / 8;
+template <int D, bool MASK, bool VEC, int TK>
+__global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
+  constexpr int NW = TK / 16;     // waves; wave w owns keys 16w..16w+15 of the tile
+  constexpr int NT = NW * 64;
+  constexpr int TQ = kBwdQueryTile, G = kBwdGroup;
+  constexpr int QP = D + 8;       // row-major Q / dO / K tile pitch (bf16)
+  constexpr int SP = TQ + 8;      // dS^T tile pitch (row = key)
+  constexpr int CH = D / 8;       // 16-byte chunks per row
   constexpr int NDB = D / 16;
+  constexpr int NQCH = TQ * CH;   // chunks of one Q (or dO) tile
   typedef typename DOp<D>::T QT;
   constexpr int QL = DOp<D>::kPerLane;
 
-  __shared__ __align__(16) uint16_t sQ[TQ * QP];
-  __shared__ __align__(16) uint16_t sdO[TQ * QP];
-  __shared__ __align__(16) uint16_t sQt[D * TP];
-  __shared__ __align__(16) uint16_t sdOt[D * TP];
-  __shared__ __align__(16) uint16_t sdS[TQ * SP];
-  __shared__ __align__(16) uint16_t sKt[G][D * KTP];
+  __shared__ __align__(16) uint16_t sQ[2][TQ * QP];
+  __shared__ __align__(16) uint16_t sdO[2][TQ * QP];
+  __shared__ __align__(16) float sL[2][TQ];    // -lse / scale of the stage's rows
+  __shared__ __align__(16) float sDl[2][TQ];   // -delta
+  __shared__ __align__(16) uint16_t sdS[2][TK * SP];
+  __shared__ __align__(16) uint16_t sK[G][TK * QP];
+  constexpr int BP = TK + 8;      // bias tile pitch (row = query)
+  __shared__ __align__(16) uint16_t sB[2][TQ * BP];
+  constexpr int NBCH = TQ * TK / 8;   // 16-byte chunks of one bias tile
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
   const int N = a.N, H = a.H, N_o = a.N_o;
-  // blockIdx.x -> (key tile t fastest, then head, outer group, example)
-  int bid = blockIdx.x;
-  const int t = bid % a.n_key_tiles; bid /= a.n_key_tiles;
-  const int h = bid % H; bid /= H;
-  const int grp = bid % a.n_groups; bid /= a.n_groups;
-  const int b = bid;
+
+  // XCD-aware order: blocks are dispatched round-robin over 8 XCDs; the key
+  // tiles of one (example, group, head) unit run on the same XCD so that they
+  // share its L2 for Q, dO and the bias rows.
+  const int nunit = a.B * a.n_groups * H;
+  const int per_xcd = (nunit + 7) / 8;
+  const int xcd = blockIdx.x % 8, kx = blockIdx.x / 8;
+  const int unit = (kx / a.n_key_tiles) * 8 + xcd;
+  if (kx / a.n_key_tiles >= per_xcd || unit >= nunit) return;
+  const int t = kx % a.n_key_tiles;
+  const int h = unit % H;
+  const int grp = (unit / H) % a.n_groups;
+  const int b = unit / (H * a.n_groups);
+
   const float scale = a.scale;
+  const float c1 = scale * kLog2e;
 
   const int key = t * TK + 16 * w + c;   // key column owned by this lane
   const bool kok = key < N;
+  const int keyc = kok ? key : N - 1;
   const uint16_t* __restrict__ Bs = a.bias + ((int64_t)b * H + h) * N * N;
 
   int nsl = N_o - grp * G;
   if (nsl > G) nsl = G;
 
-  // per-slice key operands (registers) and K^T tile (LDS), staged once
-  QT kB[G], vB[G];
-  float mk[G];
+  // per-slice key operands (registers), key mask, K tile (LDS), accumulators
+  QT vB[G];
+  float mk2[G];
   f32x4 dk_acc[G][NDB], dv_acc[G][NDB];
-  const int srow = tid / CH, sch = tid % CH;
 #pragma unroll
   for (int gs = 0; gs < G; ++gs) {
     QT z = {};
-    kB[gs] = z;
     vB[gs] = z;
-    mk[gs] = -INFINITY;
+    mk2[gs] = -INFINITY;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       dk_acc[gs][db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -77,169 +92,217 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
       const int o = grp * G + gs;
       const int64_t slice = (((int64_t)b * N_o + o) * H + h) * N;
       if (kok) {
-        kB[gs] = ld_global<QT>(a.k + (slice + key) * D + g * QL);
         vB[gs] = ld_global<QT>(a.v + (slice + key) * D + g * QL);
-        mk[gs] = MASK ? a.mask[((int64_t)b * N_o + o) * N + key] : 0.f;
+        mk2[gs] = MASK ? a.mask[((int64_t)b * N_o + o) * N + key] * kLog2e : 0.f;
       }
-      if (srow < TK) {
-        const int kr = t * TK + srow;
+      for (int ci = tid; ci < TK * CH; ci += NT) {
+        const int r = ci / CH, ch = ci % CH;
+        const int kr = t * TK + r;
         u32x4 kv = u32x4{0, 0, 0, 0};
-        if (kr < N) kv = ld_global<u32x4>(a.k + (slice + kr) * D + sch * 8);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sKt[gs][(sch * 8 + 2 * j) * KTP + srow] = (uint16_t)(kv[j] & 0xffffu);
-          sKt[gs][(sch * 8 + 2 * j + 1) * KTP + srow] = (uint16_t)(kv[j] >> 16);
-        }
+        if (kr < N) kv = ld_global<u32x4>(a.k + (slice + kr) * D + ch * 8);
+        *reinterpret_cast<u32x4*>(&sK[gs][r * QP + ch * 8]) = kv;
       }
     }
   }
 
   const int nqt = (N + TQ - 1) / TQ;
+  const int n_it = nqt * nsl;
 
-  // register prefetch of the next (query tile, slice) stage
-  u32x4 rq, rdo;
-  auto prefetch = [&](int j, int gs) {
+  // staging registers of one (query tile, slice) stage
+  constexpr int NR = (2 * NQCH + NT - 1) / NT;
+  u32x4 rq[NR];
+  f32x4 rls = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load_stage = [&](int it) {
+    const int j = it / nsl, gs = it % nsl;
     const int o = grp * G + gs;
     const int64_t slice = (((int64_t)b * N_o + o) * H + h) * N;
-    const int qr = j * TQ + srow;
-    rq = u32x4{0, 0, 0, 0};
-    rdo = u32x4{0, 0, 0, 0};
-    if (srow < TQ && qr < N) {
-      rq = ld_global<u32x4>(a.q + (slice + qr) * D + sch * 8);
-      rdo = ld_global<u32x4>(a.d_o + (slice + qr) * D + sch * 8);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int ci = tid + r * NT;
+      rq[r] = u32x4{0, 0, 0, 0};
+      if (ci < 2 * NQCH) {
+        const int which = ci / NQCH, cc = ci % NQCH;
+        const int row = cc / CH, ch = cc % CH;
+        const int q = j * TQ + row;
+        if (q < N) rq[r] = ld_global<u32x4>((which ? a.d_o : a.q) + (slice + q) * D + ch * 8);
+      }
+    }
+    if (tid < 2 * TQ / 4) {     // 16 chunks of lse, 16 of delta
+      const int which = tid / (TQ / 4), q0 = j * TQ + 4 * (tid % (TQ / 4));
+      const float* src = which ? a.delta : a.lse;
+      if (VEC && q0 + 3 < N) {
+        rls = ld_global<f32x4>(src + slice + q0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rls[i] = q0 + i < N ? src[slice + q0 + i] : 0.f;
+      }
+      // rows past N: lse = +inf (P = 0), delta = 0
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!which && q0 + i >= N) rls[i] = INFINITY;
     }
   };
-  auto stage = [&]() {
-    if (srow < TQ) {
-      *reinterpret_cast<u32x4*>(&sQ[srow * QP + sch * 8]) = rq;
-      *reinterpret_cast<u32x4*>(&sdO[srow * QP + sch * 8]) = rdo;
+  auto stage = [&](int buf) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sQt[(sch * 8 + 2 * j) * TP + srow] = (uint16_t)(rq[j] & 0xffffu);
-        sQt[(sch * 8 + 2 * j + 1) * TP + srow] = (uint16_t)(rq[j] >> 16);
-        sdOt[(sch * 8 + 2 * j) * TP + srow] = (uint16_t)(rdo[j] & 0xffffu);
-        sdOt[(sch * 8 + 2 * j + 1) * TP + srow] = (uint16_t)(rdo[j] >> 16);
+    for (int r = 0; r < NR; ++r) {
+      const int ci = tid + r * NT;
+      if (ci < 2 * NQCH) {
+        const int which = ci / NQCH, cc = ci % NQCH;
+        const int row = cc / CH, ch = cc % CH;
+        uint16_t* dst = which ? sdO[buf] : sQ[buf];
+        *reinterpret_cast<u32x4*>(&dst[row * QP + ch * 8]) = rq[r];
+      }
+    }
+    if (tid < 2 * TQ / 4) {
+      const int which = tid / (TQ / 4), q0 = 4 * (tid % (TQ / 4));
+      if (which) *reinterpret_cast<f32x4*>(&sDl[buf][q0]) = -rls;
+      else *reinterpret_cast<f32x4*>(&sL[buf][q0]) = -rls * (1.0f / scale);
+    }
+  };
+
+  // bias tile of (query tile j, key tile t), staged row-major [query][key]
+  u32x4 rbias[(NBCH + NT - 1) / NT];
+  constexpr int NRB = (NBCH + NT - 1) / NT;
+  auto load_bias = [&](int j) {
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+      const int ci = tid + r * NT;
+      rbias[r] = u32x4{0, 0, 0, 0};
+      if (ci < NBCH) {
+        const int row = ci / (TK / 8), ch = ci % (TK / 8);
+        int q = j * TQ + row;
+        q = q < N ? q : N - 1;
+        const int k0 = t * TK + ch * 8;
+        const uint16_t* src = Bs + (int64_t)q * N + k0;
+        if (VEC) {
+          // N % 8 == 0: a chunk of 8 keys is entirely in or entirely out of range
+          if (k0 < N) rbias[r] = ld_global<u32x4>(src);
+        } else {
+          uint32_t wv[4];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t lo = k0 + 2 * p < N ? (uint32_t)src[2 * p] : 0u;
+            const uint32_t hi = k0 + 2 * p + 1 < N ? (uint32_t)src[2 * p + 1] : 0u;
+            wv[p] = lo | (hi << 16);
+          }
+          rbias[r] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        }
+      }
+    }
+  };
+  auto stage_bias = [&](int bbuf) {
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+      const int ci = tid + r * NT;
+      if (ci < NBCH) {
+        const int row = ci / (TK / 8), ch = ci % (TK / 8);
+        *reinterpret_cast<u32x4*>(&sB[bbuf][row * BP + ch * 8]) = rbias[r];
       }
     }
   };
 
-  if (nsl > 0) prefetch(0, 0);
+  if (n_it > 0) {
+    load_stage(0);
+    load_bias(0);
+    stage(0);
+    stage_bias(0);
+    if (n_it > 1) load_stage(1);
+    if (nqt > 1) load_bias(1);
+  }
+  __syncthreads();
+
+  int it = 0;
   for (int j = 0; j < nqt; ++j) {
-    // bias of the lane's (query, key) pairs for query tile j, shared by the G slices
-    float bb[4][4];
+    // bias * log2(e) of the lane's (query, key) pairs: one transposing read per block
+    // gives rows 32s + 8g + 4e + 0..3 of block qb = 2s + e at the lane's key column
+    f32x4 bb[4];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = j * TQ + 32 * (qb >> 1) + 8 * g + 4 * (qb & 1) + i;
-        bb[qb][i] = (kok && q < N) ? bf_to_f(Bs[(int64_t)q * N + key]) : 0.f;
-      }
-    f32x4 dbacc[4];   // sum over the group's slices of the FP32 dS, in slice order
+    for (int qb = 0; qb < 4; ++qb) {
+      const int r0 = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);
+      const int k = (lane & 15) >> 2, aa = lane & 3;
+      const u32x2 bw = ds_read_tr(&sB[j & 1][(r0 + k) * BP + 16 * w + 4 * aa]);
+      bb[qb] = f32x4{bf_lo(bw[0]), bf_hi(bw[0]), bf_lo(bw[1]), bf_hi(bw[1])} * kLog2e;
+    }
+    f32x4 dbacc[4];         // sum over the group's slices of the FP32 dS, in slice order
 
 #pragma unroll
     for (int gs = 0; gs < G; ++gs) {
       if (gs >= nsl) break;
+      const int buf = it & 1;
       const int o = grp * G + gs;
       const int64_t slice = (((int64_t)b * N_o + o) * H + h) * N;
 
-      // per-register softmax statistics: rows 32s + 8g + 4e + 0..3 of block qb = 2s + e
-      f32x4 nlse[4], ndel[4];
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const int q0 = j * TQ + 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);
-        if (VEC) {
-          if (q0 < N) {
-            nlse[qb] = ld_global<f32x4>(a.lse + slice + q0);
-            ndel[qb] = ld_global<f32x4>(a.delta + slice + q0);
-          } else {
-            nlse[qb] = f32x4{INFINITY, INFINITY, INFINITY, INFINITY};
-            ndel[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool ok = q0 + i < N;
-            nlse[qb][i] = ok ? a.lse[slice + q0 + i] : INFINITY;
-            ndel[qb][i] = ok ? a.delta[slice + q0 + i] : 0.f;
-          }
-        }
-        nlse[qb] = -nlse[qb] * kLog2e;
-        ndel[qb] = -ndel[qb];
-      }
-
-      __syncthreads();          // previous stage's LDS readers are done
-      stage();
-      __syncthreads();          // Q, dO tiles of this stage visible
-      if (gs + 1 < nsl) prefetch(j, gs + 1);
-      else if (j + 1 < nqt) prefetch(j + 1, 0);
-
-      u32x2 pP[4], pS[4];
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const int ql = 32 * (qb >> 1) + 8 * (c >> 2) + 4 * (qb & 1) + (c & 3);
-        const QT qa = ld_shared<QT>(&sQ[ql * QP + g * QL]);
-        const QT da = ld_shared<QT>(&sdO[ql * QP + g * QL]);
-        const f32x4 s = DOp<D>::mma(qa, kB[gs], f32x4{0.f, 0.f, 0.f, 0.f});
-        const f32x4 dp = DOp<D>::mma(da, vB[gs], ndel[qb]);   // dP - delta
-        float p[4], ds[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = fmaf(s[i], scale, bb[qb][i]);
-          x += mk[gs];
-          p[i] = __builtin_amdgcn_exp2f(fmaf(x, kLog2e, nlse[qb][i]));
-          ds[i] = p[i] * dp[i];
-        }
-        if (gs == 0) {
-          dbacc[qb] = f32x4{ds[0], ds[1], ds[2], ds[3]};
-        } else {
-          dbacc[qb] += f32x4{ds[0], ds[1], ds[2], ds[3]};
-        }
-        pP[qb] = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
-        pS[qb] = u32x2{pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3])};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int qr = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1) + i;
-          const uint32_t wd = pS[qb][i >> 1];
-          sdS[qr * SP + 16 * w + c] = (uint16_t)((i & 1) ? (wd >> 16) : (wd & 0xffffu));
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS, contracting over the 64 queries in two steps
+      const QT kb = ld_shared<QT>(&sK[gs][(16 * w + c) * QP + g * QL]);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const u32x4 bp = u32x4{pP[2 * st][0], pP[2 * st][1], pP[2 * st + 1][0], pP[2 * st + 1][1]};
-        const u32x4 bs = u32x4{pS[2 * st][0], pS[2 * st][1], pS[2 * st + 1][0], pS[2 * st + 1][1]};
+        u32x2 pP[2], pS[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int qb = 2 * st + e;
+          const int ql = 32 * st + 8 * (c >> 2) + 4 * e + (c & 3);
+          const int r0 = 32 * st + 8 * g + 4 * e;
+          const QT qa = ld_shared<QT>(&sQ[buf][ql * QP + g * QL]);
+          const QT da = ld_shared<QT>(&sdO[buf][ql * QP + g * QL]);
+          const f32x4 nl = *reinterpret_cast<const f32x4*>(&sL[buf][r0]);
+          const f32x4 nd = *reinterpret_cast<const f32x4*>(&sDl[buf][r0]);
+          const f32x4 s = DOp<D>::mma(qa, kb, nl);         // q.k - lse/scale
+          const f32x4 dp = DOp<D>::mma(da, vB[gs], nd);    // dP - delta
+          float p[4], ds[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = fmaf(s[i], c1, bb[qb][i]);
+            if (MASK) x += mk2[gs];
+            p[i] = __builtin_amdgcn_exp2f(x);
+            ds[i] = p[i] * dp[i];
+          }
+          if (gs == 0) {
+            dbacc[qb] = f32x4{ds[0], ds[1], ds[2], ds[3]};
+          } else {
+            dbacc[qb] += f32x4{ds[0], ds[1], ds[2], ds[3]};
+          }
+          pP[e] = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+          pS[e] = u32x2{pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3])};
+          *reinterpret_cast<u32x2*>(&sdS[buf][(16 * w + c) * SP + r0]) = pS[e];
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries of this half
+        const u32x4 bp = u32x4{pP[0][0], pP[0][1], pP[1][0], pP[1][1]};
+        const u32x4 bs = u32x4{pS[0][0], pS[0][1], pS[1][0], pS[1][1]};
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const u32x4 ao = ld_shared<u32x4>(&sdOt[(16 * db + c) * TP + 32 * st + 8 * g]);
-          const u32x4 aq = ld_shared<u32x4>(&sQt[(16 * db + c) * TP + 32 * st + 8 * g]);
+          const u32x4 ao = ds_read_tr8<QP>(&sdO[buf][(32 * st + 8 * g) * QP + 16 * db], lane);
+          const u32x4 aq = ds_read_tr8<QP>(&sQ[buf][(32 * st + 8 * g) * QP + 16 * db], lane);
           dv_acc[gs][db] = mfma_k32(ao, bp, dv_acc[gs][db]);
           dk_acc[gs][db] = mfma_k32(aq, bs, dk_acc[gs][db]);
         }
       }
-      __syncthreads();          // the whole dS tile is in LDS
 
-      // dQ^T (queries 16w..16w+15 of the tile) = K^T dS^T over the 64 keys of this tile
-      {
-        f32x4 dq[NDB];
+      if (it + 1 < n_it) {
+        stage(buf ^ 1);
+        if (gs == nsl - 1) stage_bias((j + 1) & 1);
+      }
+      __syncthreads();          // dS^T tile complete; next stage's Q, dO (and bias) visible
+
+      // dQ^T blocks (queries 16qb.., features 16db..) = K^T dS^T over the TK keys
+      constexpr int NBLK = 4 * NDB;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) dq[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int bi = w; bi < NBLK; bi += NW) {
+        const int qb = bi / NDB, db = bi % NDB;
+        f32x4 dq = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4 bsd = ld_shared<u32x4>(&sdS[(16 * w + c) * SP + 32 * st + 8 * g]);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const u32x4 ak = ld_shared<u32x4>(&sKt[gs][(16 * db + c) * KTP + 32 * st + 8 * g]);
-            dq[db] = mfma_k32(ak, bsd, dq[db]);
-          }
+        for (int st = 0; st < TK / 32; ++st) {
+          const u32x4 ak = ds_read_tr8<QP>(&sK[gs][(32 * st + 8 * g) * QP + 16 * db], lane);
+          const u32x4 bs = ds_read_tr8<SP>(&sdS[buf][(32 * st + 8 * g) * SP + 16 * qb], lane);
+          dq = mfma_k32(ak, bs, dq);
         }
-        const int q = j * TQ + 16 * w + c;
+        const int q = j * TQ + 16 * qb + c;
         if (q < N) {
           float* dst = a.dq_partial + ((int64_t)t * a.B * N_o * H * N + slice + q) * D;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = dq[db] * scale;
+          *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = dq * scale;
         }
       }
+      if (it + 2 < n_it) load_stage(it + 2);
+      if (gs == nsl - 1 && j + 2 < nqt) load_bias(j + 2);
+      ++it;
     }
 
     if (kok) {
@@ -278,8 +341,10 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
 
 template <int D, bool MASK, bool VEC>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
-  const int64_t nblk = (int64_t)a.n_key_tiles * a.H * a.n_groups * a.B;
-  hipLaunchKernelGGL((bwd_kernel<D, MASK, VEC>), dim3((unsigned)nblk), dim3(256), 0, s, a);
+  constexpr int TK = kBwdKeyTile;
+  const int64_t nunit = (int64_t)a.B * a.n_groups * a.H;
+  const int64_t nblk = 8 * ((nunit + 7) / 8) * a.n_key_tiles;
+  hipLaunchKernelGGL((bwd_kernel<D, MASK, VEC, TK>), dim3((unsigned)nblk), dim3(TK * 4), 0, s, a);
   return hipGetLastError();
 }
 

@@ -68,6 +68,30 @@ template <typename T> __device__ __forceinline__ T ld_global(const void* p) {
   return *reinterpret_cast<const T*>(p);
 }
 
+// LDS transposing read (ds_read_b64_tr_b16).  Within each 16-lane group, lane
+// 4k + a (k, a = 0..3) supplies the address of 4 consecutive bf16 of row k of a
+// 4 x 16 block (its column chunk a); lane i of the group then receives column i
+// of the block, i.e. the four rows' elements at column i.  With rows = the
+// contraction index this yields 4 contraction slots of an MFMA operand whose
+// row/column index is the lane's position in the group.
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+// Two transposing reads = one 8-slot operand: rows r0 + 0..3 then r0 + 4..7.
+// `base` points at element (r0, col0) of a row-major bf16 tile with `pitch`
+// elements per row; the lane's own row/column chunk is added here.
+template <int PITCH>
+__device__ __forceinline__ u32x4 ds_read_tr8(const uint16_t* base, int lane) {
+  const int k = (lane & 15) >> 2, a = lane & 3;
+  const uint16_t* p = base + k * PITCH + 4 * a;
+  const u32x2 lo = ds_read_tr(p);
+  const u32x2 hi = ds_read_tr(p + 4 * PITCH);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 __device__ __forceinline__ float wave_max_groups(float x) {
   // max over the 4 lane groups that share a column (lanes c, c+16, c+32, c+48)
   x = fmaxf(x, __shfl_xor(x, 16));

@@ -10,9 +10,10 @@
 // lane owns one query column: the row statistics (max, sum) of a query live
 // in one lane plus its three partner lanes, the bias row of a query is read
 // as contiguous 16-byte chunks, and the bf16 probability block is already the
-// B operand of O^T = V^T P^T.  K and V^T tiles of 64 keys are staged in LDS
-// (double-buffered, shared by the four waves); the bias and mask of the next
-// tile are prefetched into registers while the current tile is computed.
+// B operand of O^T = V^T P^T.  K and V tiles of 64 keys are staged row-major
+// in LDS (double-buffered, shared by the four waves); the V^T operand is read
+// with the LDS transposing read.  Bias and mask of the next tile are loaded
+// into registers while the current tile is in flight.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,15 +22,14 @@ namespace tri {
 template <int D, bool MASK, bool VEC>
 __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   constexpr int TQ = kFwdQueryTile, TK = kFwdKeyTile;
-  constexpr int KP = D + 8;    // K tile pitch (bf16), one row per key
-  constexpr int VP = TK + 8;   // V^T tile pitch (bf16), one row per feature
+  constexpr int KP = D + 8;    // K / V tile pitch (bf16), one row per key
   constexpr int CH = D / 8;    // 16-byte chunks per K/V row
   constexpr int NDB = D / 16;  // 16-wide feature blocks of O
   typedef typename DOp<D>::T QT;
   constexpr int QL = DOp<D>::kPerLane;
 
   __shared__ __align__(16) uint16_t sK[2][TK * KP];
-  __shared__ __align__(16) uint16_t sV[2][D * VP];
+  __shared__ __align__(16) uint16_t sV[2][TK * KP];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
   const int N = a.N;
@@ -43,82 +43,99 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const float* __restrict__ Ms = MASK ? a.mask + (int64_t)bo * N : nullptr;
   const float scale = a.scale;
 
+  // queries of this lane; rows past N are clamped for loads and never stored
   int qrow[2];
-  bool qok[2];
+  const uint16_t* brow[2];
   QT qop[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     qrow[qb] = qt * TQ + 32 * w + 16 * qb + c;
-    qok[qb] = qrow[qb] < N;
-    QT z = {};
-    qop[qb] = qok[qb] ? ld_global<QT>(Qs + (int64_t)qrow[qb] * D + g * QL) : z;
+    const int ql = qrow[qb] < N ? qrow[qb] : N - 1;
+    qop[qb] = ld_global<QT>(Qs + (int64_t)ql * D + g * QL);
+    brow[qb] = Bs + (int64_t)ql * N;
   }
 
-  // staging of one K/V row chunk per thread
-  const int srow = tid / CH, sch = tid % CH;
+  const int srow = tid / CH, sch = tid % CH;   // staging: one 16-byte chunk of a K and a V row
   const bool sact = srow < TK;
+  const int nkt = (N + TK - 1) / TK;
+  const int nfull = N / TK;                    // tiles with every key in range
 
   u32x4 rk, rv;
   u32x4 rb[2][2];      // bias [qb][m]: keys 32m + 8g + 0..7 of the tile
   f32x4 rm[2][2];      // mask [m][e]: keys 32m + 8g + 4e + 0..3
 
-  auto prefetch = [&](int kt) {
-    const int k0 = kt * TK;
+  auto load_kv = [&](int kt) {
+    const int kr = kt * TK + srow;
     rk = u32x4{0, 0, 0, 0};
     rv = u32x4{0, 0, 0, 0};
-    if (sact && k0 + srow < N) {
-      rk = ld_global<u32x4>(Ks + (int64_t)(k0 + srow) * D + sch * 8);
-      rv = ld_global<u32x4>(Vs + (int64_t)(k0 + srow) * D + sch * 8);
+    if (sact && kr < N) {
+      rk = ld_global<u32x4>(Ks + (int64_t)kr * D + sch * 8);
+      rv = ld_global<u32x4>(Vs + (int64_t)kr * D + sch * 8);
     }
+  };
+  auto load_bm = [&](int kt) {
+    const int k0 = kt * TK;
+    if (kt < nfull) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int kk = k0 + 32 * m + 8 * g;
+      for (int m = 0; m < 2; ++m) {
+        const int kk = k0 + 32 * m + 8 * g;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        if (VEC) {
-          if (kk >= N) {
-            rb[qb][m] = u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
-          } else if (qok[qb]) {
-            rb[qb][m] = ld_global<u32x4>(Bs + (int64_t)qrow[qb] * N + kk);
+        for (int qb = 0; qb < 2; ++qb) {
+          if (VEC) {
+            rb[qb][m] = ld_global<u32x4>(brow[qb] + kk);
           } else {
-            rb[qb][m] = u32x4{0, 0, 0, 0};
+            uint32_t wv[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+              wv[p] = (uint32_t)brow[qb][kk + 2 * p] | ((uint32_t)brow[qb][kk + 2 * p + 1] << 16);
+            rb[qb][m] = u32x4{wv[0], wv[1], wv[2], wv[3]};
           }
-        } else {
+        }
+        if (MASK) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            if (VEC) {
+              rm[m][e] = ld_global<f32x4>(Ms + kk + 4 * e);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) rm[m][e][i] = Ms[kk + 4 * e + i];
+            }
+          }
+        }
+      }
+    } else {
+      // last, partial tile: keys past N get a -inf bias (bf16 0xff80)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int kk = k0 + 32 * m + 8 * g;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
           uint32_t wv[4];
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            uint32_t lo, hi;
             const int k_lo = kk + 2 * p, k_hi = kk + 2 * p + 1;
-            lo = k_lo >= N ? 0xff80u : (qok[qb] ? Bs[(int64_t)qrow[qb] * N + k_lo] : 0u);
-            hi = k_hi >= N ? 0xff80u : (qok[qb] ? Bs[(int64_t)qrow[qb] * N + k_hi] : 0u);
+            const uint32_t lo = k_lo < N ? (uint32_t)brow[qb][k_lo] : 0xff80u;
+            const uint32_t hi = k_hi < N ? (uint32_t)brow[qb][k_hi] : 0xff80u;
             wv[p] = lo | (hi << 16);
           }
           rb[qb][m] = u32x4{wv[0], wv[1], wv[2], wv[3]};
         }
-      }
-      if (MASK) {
+        if (MASK) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int k4 = kk + 4 * e;
-          if (VEC) {
-            rm[m][e] = k4 < N ? ld_global<f32x4>(Ms + k4) : f32x4{0.f, 0.f, 0.f, 0.f};
-          } else {
+          for (int e = 0; e < 2; ++e)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rm[m][e][i] = (k4 + i < N) ? Ms[k4 + i] : 0.f;
-          }
+            for (int i = 0; i < 4; ++i) {
+              const int kx = kk + 4 * e + i;
+              rm[m][e][i] = kx < N ? Ms[kx] : 0.f;
+            }
         }
       }
     }
   };
-
   auto stage = [&](int buf) {
     if (sact) {
       *reinterpret_cast<u32x4*>(&sK[buf][srow * KP + sch * 8]) = rk;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sV[buf][(sch * 8 + 2 * j) * VP + srow] = (uint16_t)(rv[j] & 0xffffu);
-        sV[buf][(sch * 8 + 2 * j + 1) * VP + srow] = (uint16_t)(rv[j] >> 16);
-      }
+      *reinterpret_cast<u32x4*>(&sV[buf][srow * KP + sch * 8]) = rv;
     }
   };
 
@@ -130,26 +147,18 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nkt = (N + TK - 1) / TK;
-  prefetch(0);
+  load_kv(0);
+  load_bm(0);
   stage(0);
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int cur = kt & 1;
-    u32x4 cb[2][2];
-    f32x4 cm[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y) {
-        cb[x][y] = rb[x][y];
-        if (MASK) cm[x][y] = rm[x][y];
-      }
-    if (kt + 1 < nkt) prefetch(kt + 1);
+    const bool more = kt + 1 < nkt;
+    if (more) load_kv(kt + 1);
 
-    // S^T blocks: rows = keys 32m + 8(r/4) + 4e + (r%4) so that lane group g
-    // holds keys 32m + 8g + 4e + 0..3 (contiguous bias/mask, contiguous V^T slots)
+    // S^T blocks: rows = keys 32m + 8(r/4) + 4e + (r%4), so that lane group g
+    // holds keys 32m + 8g + 4e + 0..3 (contiguous bias/mask, and the V^T slots)
     f32x4 sacc[2][2][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -162,6 +171,23 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
           sacc[qb][m][e] = DOp<D>::mma(ka, qop[qb], f32x4{0.f, 0.f, 0.f, 0.f});
       }
 
+    // scores in natural units: s * scale + bias (+ mask)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t wd = rb[qb][m][2 * e + (i >> 1)];
+            const float bv = (i & 1) ? bf_hi(wd) : bf_lo(wd);
+            float x = fmaf(sacc[qb][m][e][i], scale, bv);
+            if (MASK) x += rm[m][e][i];
+            sacc[qb][m][e][i] = x;
+          }
+    if (more) load_bm(kt + 1);
+
     u32x4 pp[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -171,14 +197,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t wd = cb[qb][m][2 * e + (i >> 1)];
-            const float bv = (i & 1) ? bf_hi(wd) : bf_lo(wd);
-            float x = fmaf(sacc[qb][m][e][i], scale, bv);
-            if (MASK) x += cm[m][e][i];
-            sacc[qb][m][e][i] = x;
-            tmax = fmaxf(tmax, x);
-          }
+          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sacc[qb][m][e][i]);
       tmax = wave_max_groups(tmax);
       const float mnew = fmaxf(mrun[qb], tmax);
       const float alpha = __builtin_amdgcn_exp2f((mrun[qb] - mnew) * kLog2e);
@@ -202,17 +221,17 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       }
     }
 
-    // O^T += V^T P^T (contraction over the 32 keys of group m)
+    // O^T += V^T P^T: contraction over the 32 keys of group m; V^T by transposing reads
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const u32x4 va = ld_shared<u32x4>(&sV[cur][(16 * db + c) * VP + 32 * m + 8 * g]);
+        const u32x4 va = ds_read_tr8<KP>(&sV[cur][(32 * m + 8 * g) * KP + 16 * db], lane);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma_k32(va, pp[qb][m], oacc[db][qb]);
       }
 
-    if (kt + 1 < nkt) stage(cur ^ 1);
+    if (more) stage(cur ^ 1);
     __syncthreads();
   }
 
@@ -221,7 +240,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   for (int qb = 0; qb < 2; ++qb) {
     const float l = wave_sum_groups(lsum[qb]);
     const float inv = 1.0f / l;
-    if (qok[qb]) {
+    if (qrow[qb] < N) {
       const int64_t row = slice + qrow[qb];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {

@@ -7,7 +7,7 @@ namespace tri {
 
 // Tile constants of the key-tile backward.  J_K = ceil(N / kBwdKeyTile) dQ
 // partials and L = ceil(N_o / kBwdGroup) dbias partials.
-constexpr int kBwdKeyTile = 64;
+constexpr int kBwdKeyTile = 128;
 constexpr int kBwdGroup = 4;
 constexpr int kBwdQueryTile = 64;
 constexpr int kFwdQueryTile = 128;
