@@ -17,8 +17,14 @@
 // transposing LDS read.  dS is stored key-major in LDS and read back, also
 // transposed, as the operand of dQ^T = K^T dS^T.  -lse/scale and -delta enter
 // as the accumulator inputs of the S and dP products, so the exponent costs
-// one FMA per score.  Q/dO tiles are double-buffered: one barrier per
-// (query tile, slice) stage.
+// one FMA per score.
+//
+// Pipeline: stages (query tile j, slice g) are double-buffered in LDS with one
+// barrier per stage; the dQ product of stage i runs after the score work of
+// stage i+1, so every barrier interval mixes VALU-heavy and MFMA-heavy work.
+// Global reads are raw buffer loads with per-slice extents: rows past N read
+// as zero, which makes their probabilities irrelevant (dO, Q and K are zero
+// there) without per-load bounds checks.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,9 +37,13 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int TQ = kBwdQueryTile, G = kBwdGroup;
   constexpr int QP = D + 8;       // row-major Q / dO / K tile pitch (bf16)
   constexpr int SP = TQ + 8;      // dS^T tile pitch (row = key)
+  constexpr int BP = TK + 8;      // bias tile pitch (row = query)
   constexpr int CH = D / 8;       // 16-byte chunks per row
   constexpr int NDB = D / 16;
   constexpr int NQCH = TQ * CH;   // chunks of one Q (or dO) tile
+  constexpr int NBCH = TQ * TK / 8;   // 16-byte chunks of one bias tile
+  constexpr int NR = (2 * NQCH + NT - 1) / NT;
+  constexpr int NRB = (NBCH + NT - 1) / NT;
   typedef typename DOp<D>::T QT;
   constexpr int QL = DOp<D>::kPerLane;
 
@@ -43,9 +53,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) float sDl[2][TQ];   // -delta
   __shared__ __align__(16) uint16_t sdS[2][TK * SP];
   __shared__ __align__(16) uint16_t sK[G][TK * QP];
-  constexpr int BP = TK + 8;      // bias tile pitch (row = query)
   __shared__ __align__(16) uint16_t sB[2][TQ * BP];
-  constexpr int NBCH = TQ * TK / 8;   // 16-byte chunks of one bias tile
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
   const int N = a.N, H = a.H, N_o = a.N_o;
@@ -65,16 +73,20 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
 
   const float scale = a.scale;
   const float c1 = scale * kLog2e;
-
   const int key = t * TK + 16 * w + c;   // key column owned by this lane
   const bool kok = key < N;
-  const int keyc = kok ? key : N - 1;
-  const uint16_t* __restrict__ Bs = a.bias + ((int64_t)b * H + h) * N * N;
 
   int nsl = N_o - grp * G;
   if (nsl > G) nsl = G;
+  const int nqt = (N + TQ - 1) / TQ;
+  const int n_it = nqt * nsl;
 
-  // per-slice key operands (registers), key mask, K tile (LDS), accumulators
+  // element offset of slice (b, grp*G + gs, h) in the [B, N_o, H, N] row space
+  auto slice_row = [&](int gs) -> int64_t { return (((int64_t)b * N_o + grp * G + gs) * H + h) * N; };
+  const uint32_t rowbytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t rbias = make_rsrc(a.bias + ((int64_t)b * H + h) * N * N, (uint32_t)N * N * 2);
+
+  // per-slice V operand (registers), key mask, K tile (LDS), accumulators
   QT vB[G];
   float mk2[G];
   f32x4 dk_acc[G][NDB], dv_acc[G][NDB];
@@ -89,57 +101,47 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       dv_acc[gs][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (gs < nsl) {
-      const int o = grp * G + gs;
-      const int64_t slice = (((int64_t)b * N_o + o) * H + h) * N;
+      const int64_t sr = slice_row(gs);
       if (kok) {
-        vB[gs] = ld_global<QT>(a.v + (slice + key) * D + g * QL);
-        mk2[gs] = MASK ? a.mask[((int64_t)b * N_o + o) * N + key] * kLog2e : 0.f;
+        vB[gs] = ld_global<QT>(a.v + (sr + key) * D + g * QL);
+        mk2[gs] = MASK ? a.mask[((int64_t)b * N_o + grp * G + gs) * N + key] * kLog2e : 0.f;
       }
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + sr * D, rowbytes);
       for (int ci = tid; ci < TK * CH; ci += NT) {
         const int r = ci / CH, ch = ci % CH;
-        const int kr = t * TK + r;
-        u32x4 kv = u32x4{0, 0, 0, 0};
-        if (kr < N) kv = ld_global<u32x4>(a.k + (slice + kr) * D + ch * 8);
+        const u32x4 kv = buf_ld16(rk, (uint32_t)((t * TK + r) * D + ch * 8) * 2);
         *reinterpret_cast<u32x4*>(&sK[gs][r * QP + ch * 8]) = kv;
       }
     }
   }
 
-  const int nqt = (N + TQ - 1) / TQ;
-  const int n_it = nqt * nsl;
-
-  // staging registers of one (query tile, slice) stage
-  constexpr int NR = (2 * NQCH + NT - 1) / NT;
+  // ---- staging of one (query tile, slice) stage: Q, dO, -lse/scale, -delta
   u32x4 rq[NR];
   f32x4 rls = f32x4{0.f, 0.f, 0.f, 0.f};
   auto load_stage = [&](int it) {
     const int j = it / nsl, gs = it % nsl;
-    const int o = grp * G + gs;
-    const int64_t slice = (((int64_t)b * N_o + o) * H + h) * N;
+    const int64_t sr = slice_row(gs);
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.q + sr * D, rowbytes);
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.d_o + sr * D, rowbytes);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const int ci = tid + r * NT;
-      rq[r] = u32x4{0, 0, 0, 0};
       if (ci < 2 * NQCH) {
         const int which = ci / NQCH, cc = ci % NQCH;
         const int row = cc / CH, ch = cc % CH;
-        const int q = j * TQ + row;
-        if (q < N) rq[r] = ld_global<u32x4>((which ? a.d_o : a.q) + (slice + q) * D + ch * 8);
+        const uint32_t off = (uint32_t)((j * TQ + row) * D + ch * 8) * 2;
+        rq[r] = buf_ld16(which ? rO : rQ, off);
       }
     }
-    if (tid < 2 * TQ / 4) {     // 16 chunks of lse, 16 of delta
+    if (tid < 2 * TQ / 4) {     // 16 chunks of lse, 16 of delta; rows past N read 0
       const int which = tid / (TQ / 4), q0 = j * TQ + 4 * (tid % (TQ / 4));
-      const float* src = which ? a.delta : a.lse;
-      if (VEC && q0 + 3 < N) {
-        rls = ld_global<f32x4>(src + slice + q0);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc((which ? a.delta : a.lse) + sr, (uint32_t)N * 4);
+      if (VEC) {
+        rls = __builtin_bit_cast(f32x4, buf_ld16(rs, (uint32_t)q0 * 4));
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rls[i] = q0 + i < N ? src[slice + q0 + i] : 0.f;
+        for (int i = 0; i < 4; ++i) rls[i] = __uint_as_float(buf_ld4(rs, (uint32_t)(q0 + i) * 4));
       }
-      // rows past N: lse = +inf (P = 0), delta = 0
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!which && q0 + i >= N) rls[i] = INFINITY;
     }
   };
   auto stage = [&](int buf) {
@@ -156,36 +158,32 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     if (tid < 2 * TQ / 4) {
       const int which = tid / (TQ / 4), q0 = 4 * (tid % (TQ / 4));
       if (which) *reinterpret_cast<f32x4*>(&sDl[buf][q0]) = -rls;
-      else *reinterpret_cast<f32x4*>(&sL[buf][q0]) = -rls * (1.0f / scale);
+      else *reinterpret_cast<f32x4*>(&sL[buf][q0]) = rls * (-1.0f / scale);
     }
   };
 
-  // bias tile of (query tile j, key tile t), staged row-major [query][key]
-  u32x4 rbias[(NBCH + NT - 1) / NT];
-  constexpr int NRB = (NBCH + NT - 1) / NT;
+  // ---- bias tile of (query tile j, key tile t), staged row-major [query][key]
+  u32x4 rbt[NRB];
   auto load_bias = [&](int j) {
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
       const int ci = tid + r * NT;
-      rbias[r] = u32x4{0, 0, 0, 0};
       if (ci < NBCH) {
         const int row = ci / (TK / 8), ch = ci % (TK / 8);
-        int q = j * TQ + row;
-        q = q < N ? q : N - 1;
-        const int k0 = t * TK + ch * 8;
-        const uint16_t* src = Bs + (int64_t)q * N + k0;
+        const int q = j * TQ + row, k0 = t * TK + ch * 8;
         if (VEC) {
-          // N % 8 == 0: a chunk of 8 keys is entirely in or entirely out of range
-          if (k0 < N) rbias[r] = ld_global<u32x4>(src);
+          // N % 8 == 0: a chunk of 8 keys is entirely in or out of range
+          rbt[r] = k0 < N ? buf_ld16(rbias, (uint32_t)(q * N + k0) * 2) : u32x4{0, 0, 0, 0};
         } else {
           uint32_t wv[4];
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const uint32_t lo = k0 + 2 * p < N ? (uint32_t)src[2 * p] : 0u;
-            const uint32_t hi = k0 + 2 * p + 1 < N ? (uint32_t)src[2 * p + 1] : 0u;
+            const int k_lo = k0 + 2 * p;
+            const uint32_t lo = k_lo < N ? buf_ld2(rbias, (uint32_t)(q * N + k_lo) * 2) : 0u;
+            const uint32_t hi = k_lo + 1 < N ? buf_ld2(rbias, (uint32_t)(q * N + k_lo + 1) * 2) : 0u;
             wv[p] = lo | (hi << 16);
           }
-          rbias[r] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+          rbt[r] = u32x4{wv[0], wv[1], wv[2], wv[3]};
         }
       }
     }
@@ -196,7 +194,31 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       const int ci = tid + r * NT;
       if (ci < NBCH) {
         const int row = ci / (TK / 8), ch = ci % (TK / 8);
-        *reinterpret_cast<u32x4*>(&sB[bbuf][row * BP + ch * 8]) = rbias[r];
+        *reinterpret_cast<u32x4*>(&sB[bbuf][row * BP + ch * 8]) = rbt[r];
+      }
+    }
+  };
+
+  // ---- dQ^T blocks (queries 16qb.., features 16db..) = K^T dS^T over the TK keys of stage `it`
+  auto dq_stage = [&](int it) {
+    const int buf = it & 1;
+    const int j = it / nsl, gs = it % nsl;
+    const int64_t sr = slice_row(gs);
+    constexpr int NBLK = 4 * NDB;
+#pragma unroll
+    for (int bi = w; bi < NBLK; bi += NW) {
+      const int qb = bi / NDB, db = bi % NDB;
+      f32x4 dq = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < TK / 32; ++st) {
+        const u32x4 ak = ds_read_tr8<QP>(&sK[gs][(32 * st + 8 * g) * QP + 16 * db], lane);
+        const u32x4 bs = ds_read_tr8<SP>(&sdS[buf][(32 * st + 8 * g) * SP + 16 * qb], lane);
+        dq = mfma_k32(ak, bs, dq);
+      }
+      const int q = j * TQ + 16 * qb + c;
+      if (q < N) {
+        float* dst = a.dq_partial + ((int64_t)t * a.B * N_o * H * N + sr + q) * D;
+        *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = dq * scale;
       }
     }
   };
@@ -229,8 +251,6 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     for (int gs = 0; gs < G; ++gs) {
       if (gs >= nsl) break;
       const int buf = it & 1;
-      const int o = grp * G + gs;
-      const int64_t slice = (((int64_t)b * N_o + o) * H + h) * N;
 
       const QT kb = ld_shared<QT>(&sK[gs][(16 * w + c) * QP + g * QL]);
 #pragma unroll
@@ -276,30 +296,14 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         }
       }
 
+      // dQ of the previous stage (its dS^T tile was completed at the previous barrier)
+      if (it > 0) dq_stage(it - 1);
+
       if (it + 1 < n_it) {
         stage(buf ^ 1);
         if (gs == nsl - 1) stage_bias((j + 1) & 1);
       }
-      __syncthreads();          // dS^T tile complete; next stage's Q, dO (and bias) visible
-
-      // dQ^T blocks (queries 16qb.., features 16db..) = K^T dS^T over the TK keys
-      constexpr int NBLK = 4 * NDB;
-#pragma unroll
-      for (int bi = w; bi < NBLK; bi += NW) {
-        const int qb = bi / NDB, db = bi % NDB;
-        f32x4 dq = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < TK / 32; ++st) {
-          const u32x4 ak = ds_read_tr8<QP>(&sK[gs][(32 * st + 8 * g) * QP + 16 * db], lane);
-          const u32x4 bs = ds_read_tr8<SP>(&sdS[buf][(32 * st + 8 * g) * SP + 16 * qb], lane);
-          dq = mfma_k32(ak, bs, dq);
-        }
-        const int q = j * TQ + 16 * qb + c;
-        if (q < N) {
-          float* dst = a.dq_partial + ((int64_t)t * a.B * N_o * H * N + slice + q) * D;
-          *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = dq * scale;
-        }
-      }
+      __syncthreads();          // this stage's dS^T complete; next stage's tiles visible
       if (it + 2 < n_it) load_stage(it + 2);
       if (gs == nsl - 1 && j + 2 < nqt) load_bias(j + 2);
       ++it;
@@ -317,14 +321,14 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         }
     }
   }
+  if (n_it > 0) dq_stage(n_it - 1);
 
   // epilogue: dK = scale * dK^T^T, dV
   if (kok) {
 #pragma unroll
     for (int gs = 0; gs < G; ++gs) {
       if (gs < nsl) {
-        const int o = grp * G + gs;
-        const int64_t row = (((int64_t)b * N_o + o) * H + h) * N + key;
+        const int64_t row = slice_row(gs) + key;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const f32x4 k4 = dk_acc[gs][db] * scale;
