@@ -55,7 +55,8 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) uint16_t sK[G][TK * QP];
   __shared__ __align__(16) uint16_t sB[2][TQ * BP];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int N = a.N, H = a.H, N_o = a.N_o;
 
   // XCD-aware order: blocks are dispatched round-robin over 8 XCDs; the key
@@ -115,22 +116,37 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     }
   }
 
-  // ---- staging of one (query tile, slice) stage: Q, dO, -lse/scale, -delta
+  // ---- staging of one (query tile, slice) stage: Q, dO, -lse/scale, -delta.
+  // With N % 8 == 0 the Q and dO rows go straight from memory to LDS: the padded
+  // tile is covered by whole-wave 1 KB pieces, lane l of a piece filling 16-byte
+  // slot l (slots that fall in a row's padding reload the row's first chunk).
+  constexpr int QCH = QP / 8;                    // 16-byte slots per padded row
+  constexpr int NQPIECE = TQ * QCH / 64;         // wave pieces per tile
+  static_assert(TQ * QCH % 64 == 0, "Q tile must be whole wave pieces");
   u32x4 rq[NR];
   f32x4 rls = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto load_stage = [&](int it) {
+  auto load_stage = [&](int it, int buf) {
     const int j = it / nsl, gs = it % nsl;
     const int64_t sr = slice_row(gs);
     const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.q + sr * D, rowbytes);
     const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.d_o + sr * D, rowbytes);
+    if (VEC) {
+      for (int pc = w; pc < 2 * NQPIECE; pc += NW) {
+        const int which = pc / NQPIECE, piece = pc % NQPIECE;
+        const int slot = piece * 64 + lane, row = slot / QCH, ch = slot % QCH;
+        const uint32_t off = (uint32_t)((j * TQ + row) * D + (ch < CH ? ch : 0) * 8) * 2;
+        buf_to_lds16(which ? rO : rQ, (which ? sdO[buf] : sQ[buf]) + piece * 512, off);
+      }
+    } else {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int ci = tid + r * NT;
-      if (ci < 2 * NQCH) {
-        const int which = ci / NQCH, cc = ci % NQCH;
-        const int row = cc / CH, ch = cc % CH;
-        const uint32_t off = (uint32_t)((j * TQ + row) * D + ch * 8) * 2;
-        rq[r] = buf_ld16(which ? rO : rQ, off);
+      for (int r = 0; r < NR; ++r) {
+        const int ci = tid + r * NT;
+        if (ci < 2 * NQCH) {
+          const int which = ci / NQCH, cc = ci % NQCH;
+          const int row = cc / CH, ch = cc % CH;
+          const uint32_t off = (uint32_t)((j * TQ + row) * D + ch * 8) * 2;
+          rq[r] = buf_ld16(which ? rO : rQ, off);
+        }
       }
     }
     if (tid < 2 * TQ / 4) {     // 16 chunks of lse, 16 of delta; rows past N read 0
@@ -145,14 +161,16 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     }
   };
   auto stage = [&](int buf) {
+    if (!VEC) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int ci = tid + r * NT;
-      if (ci < 2 * NQCH) {
-        const int which = ci / NQCH, cc = ci % NQCH;
-        const int row = cc / CH, ch = cc % CH;
-        uint16_t* dst = which ? sdO[buf] : sQ[buf];
-        *reinterpret_cast<u32x4*>(&dst[row * QP + ch * 8]) = rq[r];
+      for (int r = 0; r < NR; ++r) {
+        const int ci = tid + r * NT;
+        if (ci < 2 * NQCH) {
+          const int which = ci / NQCH, cc = ci % NQCH;
+          const int row = cc / CH, ch = cc % CH;
+          uint16_t* dst = which ? sdO[buf] : sQ[buf];
+          *reinterpret_cast<u32x4*>(&dst[row * QP + ch * 8]) = rq[r];
+        }
       }
     }
     if (tid < 2 * TQ / 4) {
@@ -163,18 +181,27 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   };
 
   // ---- bias tile of (query tile j, key tile t), staged row-major [query][key]
-  u32x4 rbt[NRB];
-  auto load_bias = [&](int j) {
+  constexpr int BCH = BP / 8;                    // 16-byte slots per padded bias row
+  constexpr int NBPIECE = TQ * BCH / 64;
+  static_assert(TQ * BCH % 64 == 0, "bias tile must be whole wave pieces");
+  u32x4 rbt[VEC ? 1 : NRB];
+  auto load_bias = [&](int j, int bbuf) {
+    if (VEC) {
+      for (int piece = w; piece < NBPIECE; piece += NW) {
+        const int slot = piece * 64 + lane, row = slot / BCH, ch = slot % BCH;
+        const int q = j * TQ + row, k0 = t * TK + (ch < TK / 8 ? ch : 0) * 8;
+        // N % 8 == 0: a chunk of 8 keys is entirely in or out of range; out of range
+        // chunks (and rows past N) read past the extent and land as zeros
+        const uint32_t off = k0 < N ? (uint32_t)(q * N + k0) * 2 : 0xfffffff0u;
+        buf_to_lds16(rbias, sB[bbuf] + piece * 512, off);
+      }
+    } else {
 #pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-      const int ci = tid + r * NT;
-      if (ci < NBCH) {
-        const int row = ci / (TK / 8), ch = ci % (TK / 8);
-        const int q = j * TQ + row, k0 = t * TK + ch * 8;
-        if (VEC) {
-          // N % 8 == 0: a chunk of 8 keys is entirely in or out of range
-          rbt[r] = k0 < N ? buf_ld16(rbias, (uint32_t)(q * N + k0) * 2) : u32x4{0, 0, 0, 0};
-        } else {
+      for (int r = 0; r < NRB; ++r) {
+        const int ci = tid + r * NT;
+        if (ci < NBCH) {
+          const int row = ci / (TK / 8), ch = ci % (TK / 8);
+          const int q = j * TQ + row, k0 = t * TK + ch * 8;
           uint32_t wv[4];
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
@@ -189,12 +216,14 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     }
   };
   auto stage_bias = [&](int bbuf) {
+    if (!VEC) {
 #pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-      const int ci = tid + r * NT;
-      if (ci < NBCH) {
-        const int row = ci / (TK / 8), ch = ci % (TK / 8);
-        *reinterpret_cast<u32x4*>(&sB[bbuf][row * BP + ch * 8]) = rbt[r];
+      for (int r = 0; r < NRB; ++r) {
+        const int ci = tid + r * NT;
+        if (ci < NBCH) {
+          const int row = ci / (TK / 8), ch = ci % (TK / 8);
+          *reinterpret_cast<u32x4*>(&sB[bbuf][row * BP + ch * 8]) = rbt[r];
+        }
       }
     }
   };
@@ -223,15 +252,23 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     }
   };
 
+  // register path: regs hold stage it+1 while stage it computes; direct path:
+  // stage it+1 is loaded straight into the other LDS buffer after barrier it-1
   if (n_it > 0) {
-    load_stage(0);
-    load_bias(0);
+    load_stage(0, 0);
+    load_bias(0, 0);
     stage(0);
     stage_bias(0);
-    if (n_it > 1) load_stage(1);
-    if (nqt > 1) load_bias(1);
+    if (!VEC) {
+      if (n_it > 1) load_stage(1, 1);
+      if (nqt > 1) load_bias(1, 1);
+    }
   }
   __syncthreads();
+  if (VEC) {
+    if (n_it > 1) load_stage(1, 1);
+    if (nqt > 1 && nsl == 1) load_bias(1, 1);
+  }
 
   int it = 0;
   for (int j = 0; j < nqt; ++j) {
@@ -303,9 +340,20 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         stage(buf ^ 1);
         if (gs == nsl - 1) stage_bias((j + 1) & 1);
       }
+      // the direct LDS loads of the next stage were issued by this wave after the
+      // previous barrier; they must land before any wave reads them
+      if (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
       __syncthreads();          // this stage's dS^T complete; next stage's tiles visible
-      if (it + 2 < n_it) load_stage(it + 2);
-      if (gs == nsl - 1 && j + 2 < nqt) load_bias(j + 2);
+      if (VEC) {
+        // stage it+2 goes into the buffer stage it just released; the bias of tile
+        // j+1 (needed after the last stage of tile j) is fetched one stage ahead
+        if (it + 2 < n_it) load_stage(it + 2, buf);
+        if (j + 1 < nqt && gs == (nsl >= 2 ? nsl - 2 : 0) && !(nsl == 1)) load_bias(j + 1, (j + 1) & 1);
+        if (nsl == 1 && j + 2 < nqt) load_bias(j + 2, j & 1);
+      } else {
+        if (it + 2 < n_it) load_stage(it + 2, 0);
+        if (gs == nsl - 1 && j + 2 < nqt) load_bias(j + 2, 0);
+      }
       ++it;
     }
 

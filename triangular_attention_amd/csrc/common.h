@@ -79,6 +79,13 @@ __device__ __forceinline__ uint16_t buf_ld2(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
+// Buffer -> LDS direct load: lane l's 16 bytes at byte offset `off` land at
+// LDS address `lds + 16 * l` (the LDS address must be wave-uniform).
+__device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 16, off, 0,
+                                           0, 0);
+}
+
 template <typename T> __device__ __forceinline__ T ld_shared(const uint16_t* p) {
   return *reinterpret_cast<const T*>(p);
 }
