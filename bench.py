@@ -38,6 +38,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, also run a plain device copy of this many bytes (3 times): the "
+                         "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write a markdown summary of a rocprofv3 --kernel-trace --stats output dir and exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn FETCH_SIZE / WRITE_SIZE counter runs into per-launch bytes and exit")
+    ap.add_argument("--command", default="", help="the command line that produced the profile (recorded)")
+    ap.add_argument("--out", default="", help="output file of the summarize modes")
     return ap.parse_args()
 
 
@@ -89,8 +98,87 @@ def cpu_baseline(w, seconds):
             "seconds": t, "slices": s, "threads_note": "BLAS threads (numpy elementwise ops run on one core)"}
 
 
+def _short_kernel_name(name):
+    name = name.replace("void ", "")
+    for k in ("fwd_kernel", "bwd_kernel", "delta_kernel", "reduce_kernel"):
+        if "tri::" + k in name:
+            return name.split("(")[0].replace("tri::", "")
+    if "copy" in name.lower() or "elementwise" in name.lower():
+        return "copy:" + name.split("(")[0][-60:]
+    return name.split("(")[0][-60:]
+
+
+def summarize_trace(d, command, out):
+    """Markdown table from rocprofv3 --kernel-trace --stats (kernel_stats.csv)."""
+    import csv
+    import glob
+    f = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    if not f:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(f[0])))
+    lines = ["# rocprofv3 kernel-trace summary", "", f"Command: `{command}`", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| {} | {} | {:.1f} | {:.1f} | {:.1f} | {:.1f}% |".format(
+            _short_kernel_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    txt = "\n".join(lines) + "\n"
+    if out:
+        open(out, "w").write(txt)
+    print(txt)
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, copy_bytes, command, out):
+    """Per-launch HBM bytes of every kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the plain copy of copy_bytes bytes."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        f = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+        vals = {}
+        for r in csv.DictReader(open(f[0])):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(_short_kernel_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    copy_k = [k for k in fetch if k.startswith("copy:")]
+    if not copy_k:
+        raise SystemExit("no copy kernel in the counter runs (run bench.py with --copy-bytes)")
+    ck = max(copy_k, key=lambda k: max(fetch[k]))
+    # the copy reads copy_bytes and writes copy_bytes
+    f_scale = copy_bytes / (max(fetch[ck]) * 1024.0)
+    w_scale = copy_bytes / (max(write[ck]) * 1024.0)
+    res = {"workload": workload, "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+           "kernel_hash": kernel_hash(), "command": command, "kernels": {}}
+    for k in fetch:
+        if k.startswith("copy:"):
+            continue
+        fb = sorted(fetch[k])[len(fetch[k]) // 2] * 1024.0 * f_scale
+        wb = sorted(write.get(k, [0.0]))[len(write.get(k, [0.0])) // 2] * 1024.0 * w_scale
+        res["kernels"][k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+    txt = json.dumps(res, indent=1)
+    if out:
+        old = {}
+        if os.path.exists(out):
+            old = json.load(open(out))
+        old[workload] = res
+        open(out, "w").write(json.dumps(old, indent=1) + "\n")
+    print(txt)
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.command, args.out)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.copy_bytes,
+                      args.command, args.out)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is described in DESIGN.md but not built).", file=sys.stderr)
@@ -175,12 +263,15 @@ def main():
                       "alg_gbs": round(alg[n]["bytes"] / (ms * 1e-3) / 1e9, 1) if ms > 0 else None}
     dom = max(KERNELS, key=lambda n: per[n])
     traffic = None
+    traffic_all = None
     if os.path.exists(args.traffic):
         try:
-            tr = json.load(open(args.traffic))
-            entry = tr.get(w.name, {}).get(dom)
-            if entry and entry.get("kernel_hash") == kernel_hash():
-                traffic = entry.get("bytes_per_launch")
+            tr = json.load(open(args.traffic)).get(w.name, {})
+            if tr.get("kernel_hash") == kernel_hash():
+                traffic_all = tr["kernels"]
+                for kname, v in traffic_all.items():
+                    if kname.startswith(dom + "_kernel"):
+                        traffic = round(v["bytes_per_launch"])
         except Exception:
             traffic = None
     if dom in ("bwd", "fwd"):
@@ -219,6 +310,16 @@ def main():
         "wall_s_timed": round(t_wall, 4),
         "gpu": torch.cuda.get_device_name(0),
     }
+    if traffic_all is not None:
+        out["traffic_bytes_per_launch"] = {k: round(v["bytes_per_launch"]) for k, v in traffic_all.items()}
+    if args.copy_bytes > 0:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = args.copy_bytes
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out))
