@@ -117,17 +117,34 @@ __device__ __forceinline__ u32x4 ds_read_tr8(const uint16_t* base, int lane) {
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-__device__ __forceinline__ float wave_max_groups(float x) {
-  // max over the 4 lane groups that share a column (lanes c, c+16, c+32, c+48)
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Cross-group exchange with VALU lane swaps (no LDS): v_permlane16_swap pairs
+// rows 0<->1 and 2<->3 of 16 lanes, v_permlane32_swap pairs the two halves;
+// with both operands equal to x the two results hold x of lane l and of lane
+// l^16 (resp. l^32) in some order.
+__device__ __forceinline__ float xor16_pair_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float wave_sum_groups(float x) {
-  // fixed order: every lane ends with (x0 + x1) + (x2 + x3), commutative adds only
-  x = x + __shfl_xor(x, 16);
-  x = x + __shfl_xor(x, 32);
-  return x;
+__device__ __forceinline__ float xor32_pair_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float xor16_pair_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_pair_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// max over the 4 lane groups that share a column (lanes c, c+16, c+32, c+48)
+__device__ __forceinline__ float wave_max_groups(float x) { return xor32_pair_max(xor16_pair_max(x)); }
+// fixed order: every lane ends with (x0 + x1) + (x2 + x3) (group sums in row order)
+__device__ __forceinline__ float wave_sum_groups(float x) { return xor32_pair_sum(xor16_pair_sum(x)); }
 
 }  // namespace tri
