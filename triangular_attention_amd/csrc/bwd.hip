@@ -24,39 +24,74 @@
 // stage i+1, so every barrier interval mixes VALU-heavy and MFMA-heavy work.
 // Global reads are raw buffer loads with per-slice extents: rows past N read
 // as zero, which makes their probabilities irrelevant (dO, Q and K are zero
-// there) without per-load bounds checks.
+// there) without per-load bounds checks.  With N % 8 == 0 the Q, dO and bias
+// tiles go from memory straight into LDS.
+//
+// LDS layouts (D = 32): Q, dO and K tiles are unpadded 64-byte rows whose four
+// 16-byte chunks are permuted by an XOR with a row-dependent value, chosen so
+// that both the row reads of the score products (16 rows, one chunk) and the
+// transposing reads (4 rows x 32 bytes per 16 lanes) touch distinct banks.
 #include "common.h"
 #include "kernels.h"
 
 namespace tri {
+
+// Element offset of (row, col) in the LDS tiles.  D = 32: unpadded rows, chunk
+// XOR swizzle; Q/dO use a swizzle of row bits 3-4 (rows 8 apart differ), K of
+// row bits 2-3 (rows 4 apart differ).  D = 16: rows padded to 24 elements.
+template <int D> struct Lay;
+template <> struct Lay<32> {
+  static constexpr int kRowElems = 32;
+  __device__ static __forceinline__ int swq(int row) { return ((row >> 3) & 1) << 1 | ((row >> 4) & 1); }
+  __device__ static __forceinline__ int swk(int row) { return (row >> 2) & 3; }
+  __device__ static __forceinline__ int q(int row, int col) {
+    return row * 32 + ((((col >> 3) ^ swq(row)) & 3) << 3) + (col & 7);
+  }
+  __device__ static __forceinline__ int k(int row, int col) {
+    return row * 32 + ((((col >> 3) ^ swk(row)) & 3) << 3) + (col & 7);
+  }
+  // logical chunk stored in physical slot `pchunk` of `row`
+  __device__ static __forceinline__ int q_src_chunk(int row, int pchunk) { return (pchunk ^ swq(row)) & 3; }
+  static constexpr int kSlotsPerRow = 4;
+};
+template <> struct Lay<16> {
+  static constexpr int kRowElems = 24;
+  __device__ static __forceinline__ int q(int row, int col) { return row * 24 + col; }
+  __device__ static __forceinline__ int k(int row, int col) { return row * 24 + col; }
+  __device__ static __forceinline__ int q_src_chunk(int row, int pchunk) { return pchunk < 2 ? pchunk : 0; }
+  static constexpr int kSlotsPerRow = 3;     // two data chunks and one padding chunk
+};
 
 template <int D, bool MASK, bool VEC, int TK>
 __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int NW = TK / 16;     // waves; wave w owns keys 16w..16w+15 of the tile
   constexpr int NT = NW * 64;
   constexpr int TQ = kBwdQueryTile, G = kBwdGroup;
-  constexpr int QP = D + 8;       // row-major Q / dO / K tile pitch (bf16)
+  constexpr int RE = Lay<D>::kRowElems;   // LDS elements per Q / dO / K row
   constexpr int SP = TQ + 8;      // dS^T tile pitch (row = key)
   constexpr int BP = TK + 8;      // bias tile pitch (row = query)
-  constexpr int CH = D / 8;       // 16-byte chunks per row
+  constexpr int CH = D / 8;       // 16-byte chunks per row in memory
   constexpr int NDB = D / 16;
   constexpr int NQCH = TQ * CH;   // chunks of one Q (or dO) tile
   constexpr int NBCH = TQ * TK / 8;   // 16-byte chunks of one bias tile
   constexpr int NR = (2 * NQCH + NT - 1) / NT;
   constexpr int NRB = (NBCH + NT - 1) / NT;
+  constexpr int NBLK = 4 * NDB;   // dQ output blocks per stage
+  static_assert(NBLK <= NW, "one dQ block per wave at most");
   typedef typename DOp<D>::T QT;
   constexpr int QL = DOp<D>::kPerLane;
 
-  __shared__ __align__(16) uint16_t sQ[2][TQ * QP];
-  __shared__ __align__(16) uint16_t sdO[2][TQ * QP];
+  __shared__ __align__(16) uint16_t sQ[2][TQ * RE];
+  __shared__ __align__(16) uint16_t sdO[2][TQ * RE];
   __shared__ __align__(16) float sL[2][TQ];    // -lse / scale of the stage's rows
   __shared__ __align__(16) float sDl[2][TQ];   // -delta
   __shared__ __align__(16) uint16_t sdS[2][TK * SP];
-  __shared__ __align__(16) uint16_t sK[G][TK * QP];
+  __shared__ __align__(16) uint16_t sK[G][TK * RE];
   __shared__ __align__(16) uint16_t sB[2][TQ * BP];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  const int trk = (lane & 15) >> 2, tra = lane & 3;         // transposing-read row / chunk of the lane
   const int N = a.N, H = a.H, N_o = a.N_o;
 
   // XCD-aware order: blocks are dispatched round-robin over 8 XCDs; the key
@@ -82,8 +117,10 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   const int nqt = (N + TQ - 1) / TQ;
   const int n_it = nqt * nsl;
 
-  // element offset of slice (b, grp*G + gs, h) in the [B, N_o, H, N] row space
-  auto slice_row = [&](int gs) -> int64_t { return (((int64_t)b * N_o + grp * G + gs) * H + h) * N; };
+  // rows of slice (b, grp*G + gs, h) start at row0 + gs * ostride in the [B, N_o, H, N] row space
+  const int64_t row0 = (((int64_t)b * N_o + grp * G) * H + h) * N;
+  const int64_t ostride = (int64_t)H * N;
+  const int64_t part_rows = (int64_t)a.B * N_o * H * N;    // rows of one dQ partial
   const uint32_t rowbytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rbias = make_rsrc(a.bias + ((int64_t)b * H + h) * N * N, (uint32_t)N * N * 2);
 
@@ -102,7 +139,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       dv_acc[gs][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (gs < nsl) {
-      const int64_t sr = slice_row(gs);
+      const int64_t sr = row0 + gs * ostride;
       if (kok) {
         vB[gs] = ld_global<QT>(a.v + (sr + key) * D + g * QL);
         mk2[gs] = MASK ? a.mask[((int64_t)b * N_o + grp * G + gs) * N + key] * kLog2e : 0.f;
@@ -111,30 +148,29 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       for (int ci = tid; ci < TK * CH; ci += NT) {
         const int r = ci / CH, ch = ci % CH;
         const u32x4 kv = buf_ld16(rk, (uint32_t)((t * TK + r) * D + ch * 8) * 2);
-        *reinterpret_cast<u32x4*>(&sK[gs][r * QP + ch * 8]) = kv;
+        *reinterpret_cast<u32x4*>(&sK[gs][Lay<D>::k(r, ch * 8)]) = kv;
       }
     }
   }
 
-  // ---- staging of one (query tile, slice) stage: Q, dO, -lse/scale, -delta.
-  // With N % 8 == 0 the Q and dO rows go straight from memory to LDS: the padded
-  // tile is covered by whole-wave 1 KB pieces, lane l of a piece filling 16-byte
-  // slot l (slots that fall in a row's padding reload the row's first chunk).
-  constexpr int QCH = QP / 8;                    // 16-byte slots per padded row
-  constexpr int NQPIECE = TQ * QCH / 64;         // wave pieces per tile
-  static_assert(TQ * QCH % 64 == 0, "Q tile must be whole wave pieces");
+  // ---- staging of one (query tile jj, slice gg) stage: Q, dO, -lse/scale, -delta.
+  // Direct path (N % 8 == 0): the tile is covered by whole-wave 1 KB pieces; lane l of
+  // a piece fills 16-byte LDS slot l, loading the logical chunk that the layout
+  // stores there (padding slots of the D = 16 layout reload chunk 0).
+  constexpr int SPR = Lay<D>::kSlotsPerRow;
+  constexpr int NQPIECE = TQ * SPR / 64;
+  static_assert(TQ * SPR % 64 == 0, "Q tile must be whole wave pieces");
   u32x4 rq[NR];
   f32x4 rls = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto load_stage = [&](int it, int buf) {
-    const int j = it / nsl, gs = it % nsl;
-    const int64_t sr = slice_row(gs);
+  auto load_stage = [&](int jj, int gg, int buf) {
+    const int64_t sr = row0 + gg * ostride;
     const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.q + sr * D, rowbytes);
     const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.d_o + sr * D, rowbytes);
     if (VEC) {
       for (int pc = w; pc < 2 * NQPIECE; pc += NW) {
-        const int which = pc / NQPIECE, piece = pc % NQPIECE;
-        const int slot = piece * 64 + lane, row = slot / QCH, ch = slot % QCH;
-        const uint32_t off = (uint32_t)((j * TQ + row) * D + (ch < CH ? ch : 0) * 8) * 2;
+        const int which = pc >= NQPIECE, piece = which ? pc - NQPIECE : pc;
+        const int slot = piece * 64 + lane, row = slot / SPR, ch = Lay<D>::q_src_chunk(row, slot % SPR);
+        const uint32_t off = (uint32_t)((jj * TQ + row) * D + ch * 8) * 2;
         buf_to_lds16(which ? rO : rQ, (which ? sdO[buf] : sQ[buf]) + piece * 512, off);
       }
     } else {
@@ -144,13 +180,13 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         if (ci < 2 * NQCH) {
           const int which = ci / NQCH, cc = ci % NQCH;
           const int row = cc / CH, ch = cc % CH;
-          const uint32_t off = (uint32_t)((j * TQ + row) * D + ch * 8) * 2;
+          const uint32_t off = (uint32_t)((jj * TQ + row) * D + ch * 8) * 2;
           rq[r] = buf_ld16(which ? rO : rQ, off);
         }
       }
     }
     if (tid < 2 * TQ / 4) {     // 16 chunks of lse, 16 of delta; rows past N read 0
-      const int which = tid / (TQ / 4), q0 = j * TQ + 4 * (tid % (TQ / 4));
+      const int which = tid / (TQ / 4), q0 = jj * TQ + 4 * (tid % (TQ / 4));
       const __amdgpu_buffer_rsrc_t rs = make_rsrc((which ? a.delta : a.lse) + sr, (uint32_t)N * 4);
       if (VEC) {
         rls = __builtin_bit_cast(f32x4, buf_ld16(rs, (uint32_t)q0 * 4));
@@ -169,7 +205,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
           const int which = ci / NQCH, cc = ci % NQCH;
           const int row = cc / CH, ch = cc % CH;
           uint16_t* dst = which ? sdO[buf] : sQ[buf];
-          *reinterpret_cast<u32x4*>(&dst[row * QP + ch * 8]) = rq[r];
+          *reinterpret_cast<u32x4*>(&dst[Lay<D>::q(row, ch * 8)]) = rq[r];
         }
       }
     }
@@ -228,49 +264,51 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     }
   };
 
-  // ---- dQ^T blocks (queries 16qb.., features 16db..) = K^T dS^T over the TK keys of stage `it`
-  auto dq_stage = [&](int it) {
-    const int buf = it & 1;
-    const int j = it / nsl, gs = it % nsl;
-    const int64_t sr = slice_row(gs);
-    constexpr int NBLK = 4 * NDB;
-#pragma unroll
-    for (int bi = w; bi < NBLK; bi += NW) {
-      const int qb = bi / NDB, db = bi % NDB;
-      f32x4 dq = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ---- dQ^T block (queries 16qb.., features 16db..) = K^T dS^T over the TK keys of a stage;
+  // wave w computes block w
+  auto dq_stage = [&](int jj, int gg, int buf) {
+    if (w < NBLK) {
+      const int qb = w / NDB, db = w % NDB;
+      const uint16_t* kt_tile = sK[gg];
+      f32x4 dq0 = f32x4{0.f, 0.f, 0.f, 0.f}, dq1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < TK / 32; ++st) {
-        const u32x4 ak = ds_read_tr8<QP>(&sK[gs][(32 * st + 8 * g) * QP + 16 * db], lane);
-        const u32x4 bs = ds_read_tr8<SP>(&sdS[buf][(32 * st + 8 * g) * SP + 16 * qb], lane);
-        dq = mfma_k32(ak, bs, dq);
+        const int kr = 32 * st + 8 * g + trk;
+        const int kc = 16 * db + 4 * tra;
+        const u32x4 ak = ds_read_tr8_at(kt_tile, Lay<D>::k(kr, kc), Lay<D>::k(kr + 4, kc));
+        const int so = (32 * st + 8 * g + trk) * SP + 16 * qb + 4 * tra;
+        const u32x4 bs = ds_read_tr8_at(sdS[buf], so, so + 4 * SP);
+        if (st & 1) dq1 = mfma_k32(ak, bs, dq1);
+        else dq0 = mfma_k32(ak, bs, dq0);
       }
-      const int q = j * TQ + 16 * qb + c;
+      const int q = jj * TQ + 16 * qb + c;
       if (q < N) {
-        float* dst = a.dq_partial + ((int64_t)t * a.B * N_o * H * N + sr + q) * D;
-        *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = dq * scale;
+        float* dst = a.dq_partial + (t * part_rows + row0 + gg * ostride + q) * D;
+        *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = (dq0 + dq1) * scale;
       }
     }
   };
 
   // register path: regs hold stage it+1 while stage it computes; direct path:
-  // stage it+1 is loaded straight into the other LDS buffer after barrier it-1
+  // stage it+2 is loaded straight into the LDS buffer that stage it releases
   if (n_it > 0) {
-    load_stage(0, 0);
+    load_stage(0, 0, 0);
     load_bias(0, 0);
     stage(0);
     stage_bias(0);
     if (!VEC) {
-      if (n_it > 1) load_stage(1, 1);
+      if (n_it > 1) load_stage(nsl > 1 ? 0 : 1, nsl > 1 ? 1 : 0, 1);
       if (nqt > 1) load_bias(1, 1);
     }
   }
   __syncthreads();
   if (VEC) {
-    if (n_it > 1) load_stage(1, 1);
+    if (n_it > 1) load_stage(nsl > 1 ? 0 : 1, nsl > 1 ? 1 : 0, 1);
     if (nqt > 1 && nsl == 1) load_bias(1, 1);
   }
 
   int it = 0;
+  int jp = 0, gp = 0;       // the previous stage (its dQ product is still pending)
   for (int j = 0; j < nqt; ++j) {
     // bias * log2(e) of the lane's (query, key) pairs: one transposing read per block
     // gives rows 32s + 8g + 4e + 0..3 of block qb = 2s + e at the lane's key column
@@ -278,8 +316,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const int r0 = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);
-      const int k = (lane & 15) >> 2, aa = lane & 3;
-      const u32x2 bw = ds_read_tr(&sB[j & 1][(r0 + k) * BP + 16 * w + 4 * aa]);
+      const u32x2 bw = ds_read_tr(&sB[j & 1][(r0 + trk) * BP + 16 * w + 4 * tra]);
       bb[qb] = f32x4{bf_lo(bw[0]), bf_hi(bw[0]), bf_lo(bw[1]), bf_hi(bw[1])} * kLog2e;
     }
     f32x4 dbacc[4];         // sum over the group's slices of the FP32 dS, in slice order
@@ -288,8 +325,10 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     for (int gs = 0; gs < G; ++gs) {
       if (gs >= nsl) break;
       const int buf = it & 1;
+      const uint16_t* tq = sQ[buf];
+      const uint16_t* tdo = sdO[buf];
 
-      const QT kb = ld_shared<QT>(&sK[gs][(16 * w + c) * QP + g * QL]);
+      const QT kb = ld_shared<QT>(&sK[gs][Lay<D>::k(16 * w + c, g * QL)]);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         u32x2 pP[2], pS[2];
@@ -298,8 +337,8 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
           const int qb = 2 * st + e;
           const int ql = 32 * st + 8 * (c >> 2) + 4 * e + (c & 3);
           const int r0 = 32 * st + 8 * g + 4 * e;
-          const QT qa = ld_shared<QT>(&sQ[buf][ql * QP + g * QL]);
-          const QT da = ld_shared<QT>(&sdO[buf][ql * QP + g * QL]);
+          const QT qa = ld_shared<QT>(&tq[Lay<D>::q(ql, g * QL)]);
+          const QT da = ld_shared<QT>(&tdo[Lay<D>::q(ql, g * QL)]);
           const f32x4 nl = *reinterpret_cast<const f32x4*>(&sL[buf][r0]);
           const f32x4 nd = *reinterpret_cast<const f32x4*>(&sDl[buf][r0]);
           const f32x4 s = DOp<D>::mma(qa, kb, nl);         // q.k - lse/scale
@@ -326,15 +365,17 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         const u32x4 bs = u32x4{pS[0][0], pS[0][1], pS[1][0], pS[1][1]};
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const u32x4 ao = ds_read_tr8<QP>(&sdO[buf][(32 * st + 8 * g) * QP + 16 * db], lane);
-          const u32x4 aq = ds_read_tr8<QP>(&sQ[buf][(32 * st + 8 * g) * QP + 16 * db], lane);
+          const int qr = 32 * st + 8 * g + trk, qc = 16 * db + 4 * tra;
+          const int olo = Lay<D>::q(qr, qc), ohi = Lay<D>::q(qr + 4, qc);
+          const u32x4 ao = ds_read_tr8_at(tdo, olo, ohi);
+          const u32x4 aq = ds_read_tr8_at(tq, olo, ohi);
           dv_acc[gs][db] = mfma_k32(ao, bp, dv_acc[gs][db]);
           dk_acc[gs][db] = mfma_k32(aq, bs, dk_acc[gs][db]);
         }
       }
 
       // dQ of the previous stage (its dS^T tile was completed at the previous barrier)
-      if (it > 0) dq_stage(it - 1);
+      if (it > 0) dq_stage(jp, gp, buf ^ 1);
 
       if (it + 1 < n_it) {
         stage(buf ^ 1);
@@ -344,16 +385,24 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       // previous barrier; they must land before any wave reads them
       if (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
       __syncthreads();          // this stage's dS^T complete; next stage's tiles visible
+
+      // stage it+2, two steps ahead in (query tile, slice) order
+      const bool last1 = gs + 1 >= nsl;
+      const int g1 = last1 ? 0 : gs + 1, j1 = last1 ? j + 1 : j;
+      const bool last2 = g1 + 1 >= nsl;
+      const int g2 = last2 ? 0 : g1 + 1, j2 = last2 ? j1 + 1 : j1;
       if (VEC) {
         // stage it+2 goes into the buffer stage it just released; the bias of tile
         // j+1 (needed after the last stage of tile j) is fetched one stage ahead
-        if (it + 2 < n_it) load_stage(it + 2, buf);
-        if (j + 1 < nqt && gs == (nsl >= 2 ? nsl - 2 : 0) && !(nsl == 1)) load_bias(j + 1, (j + 1) & 1);
+        if (it + 2 < n_it) load_stage(j2, g2, buf);
+        if (j + 1 < nqt && nsl >= 2 && gs == nsl - 2) load_bias(j + 1, (j + 1) & 1);
         if (nsl == 1 && j + 2 < nqt) load_bias(j + 2, j & 1);
       } else {
-        if (it + 2 < n_it) load_stage(it + 2, 0);
+        if (it + 2 < n_it) load_stage(j2, g2, 0);
         if (gs == nsl - 1 && j + 2 < nqt) load_bias(j + 2, 0);
       }
+      jp = j;
+      gp = gs;
       ++it;
     }
 
@@ -369,14 +418,14 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         }
     }
   }
-  if (n_it > 0) dq_stage(n_it - 1);
+  if (n_it > 0) dq_stage(jp, gp, (n_it - 1) & 1);
 
   // epilogue: dK = scale * dK^T^T, dV
   if (kok) {
 #pragma unroll
     for (int gs = 0; gs < G; ++gs) {
       if (gs < nsl) {
-        const int64_t row = slice_row(gs) + key;
+        const int64_t row = row0 + gs * ostride + key;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const f32x4 k4 = dk_acc[gs][db] * scale;

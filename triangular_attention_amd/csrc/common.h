@@ -142,6 +142,14 @@ __device__ __forceinline__ float xor32_pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Two transposing reads at explicit element offsets (rows r0 + 0..3 and
+// r0 + 4..7 of the lane's column chunk), for tiles with a swizzled layout.
+__device__ __forceinline__ u32x4 ds_read_tr8_at(const uint16_t* tile, int off_lo, int off_hi) {
+  const u32x2 lo = ds_read_tr(tile + off_lo);
+  const u32x2 hi = ds_read_tr(tile + off_hi);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 // max over the 4 lane groups that share a column (lanes c, c+16, c+32, c+48)
 __device__ __forceinline__ float wave_max_groups(float x) { return xor32_pair_max(xor16_pair_max(x)); }
 // fixed order: every lane ends with (x0 + x1) + (x2 + x3) (group sums in row order)
