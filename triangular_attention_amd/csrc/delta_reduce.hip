@@ -40,16 +40,39 @@ __global__ __launch_bounds__(256) void delta_kernel(DeltaArgs a) {
   if (row < a.rows && part == 0) a.delta[row] = acc;
 }
 
-// out[i] = bf16(sum_{p=0..P-1} partial[p][i]), p ascending; 4 elements per thread.
+// out[i] = bf16(sum_{p=0..P-1} partial[p][i]), p ascending.  Each thread owns 8
+// consecutive elements and fetches up to 8 partials at a time (independent
+// loads in flight), then adds them strictly in index order.  The partials are
+// read once: nontemporal loads.
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
-  const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (i4 >= a.elems) return;
-  if (i4 + 4 <= a.elems && (a.elems % 4) == 0) {
-    f32x4 acc = ld_global<f32x4>(a.partial + i4);
-    for (int p = 1; p < a.n_partials; ++p) acc += ld_global<f32x4>(a.partial + (int64_t)p * a.elems + i4);
-    *reinterpret_cast<u32x2*>(a.out + i4) = u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+  const int64_t i8 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (i8 >= a.elems) return;
+  if (i8 + 8 <= a.elems && (a.elems % 4) == 0) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.partial + i8);
+    const int64_t pstride = a.elems / 4;        // in f32x4 units
+    f32x4 acc0 = __builtin_nontemporal_load(src), acc1 = __builtin_nontemporal_load(src + 1);
+    int p = 1;
+    for (; p + 8 <= a.n_partials; p += 8) {
+      f32x4 x0[8], x1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        x0[u] = __builtin_nontemporal_load(src + (p + u) * pstride);
+        x1[u] = __builtin_nontemporal_load(src + (p + u) * pstride + 1);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc0 += x0[u];
+        acc1 += x1[u];
+      }
+    }
+    for (; p < a.n_partials; ++p) {
+      acc0 += __builtin_nontemporal_load(src + p * pstride);
+      acc1 += __builtin_nontemporal_load(src + p * pstride + 1);
+    }
+    *reinterpret_cast<u32x4*>(a.out + i8) = u32x4{pack_bf16(acc0[0], acc0[1]), pack_bf16(acc0[2], acc0[3]),
+                                                  pack_bf16(acc1[0], acc1[1]), pack_bf16(acc1[2], acc1[3])};
   } else {
-    for (int64_t i = i4; i < i4 + 4 && i < a.elems; ++i) {
+    for (int64_t i = i8; i < i8 + 8 && i < a.elems; ++i) {
       float acc = a.partial[i];
       for (int p = 1; p < a.n_partials; ++p) acc += a.partial[(int64_t)p * a.elems + i];
       a.out[i] = f_to_bf(acc);
@@ -73,7 +96,7 @@ hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t s) {
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
-  const int64_t threads = (a.elems + 3) / 4;
+  const int64_t threads = (a.elems + 7) / 8;
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
