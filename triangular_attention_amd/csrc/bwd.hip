@@ -20,8 +20,9 @@
 // one FMA per score.
 //
 // Pipeline: stages (query tile j, slice g) are double-buffered in LDS with one
-// barrier per stage; the dQ product of stage i runs after the score work of
-// stage i+1, so every barrier interval mixes VALU-heavy and MFMA-heavy work.
+// barrier per stage; the dQ product of stage i runs in stage i+1, in the same
+// straight-line block as that stage's score work, so every barrier interval
+// mixes VALU-heavy and MFMA-heavy work.
 // Global reads are raw buffer loads with per-slice extents: rows past N read
 // as zero, which makes their probabilities irrelevant (dO, Q and K are zero
 // there) without per-load bounds checks.  With N % 8 == 0 the Q, dO and bias
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
 
   // ---- dQ^T block (queries 16qb.., features 16db..) = K^T dS^T over the TK keys of a stage;
   // wave w computes block w
-  auto dq_stage = [&](int jj, int gg, int buf) {
+  auto dq_stage = [&](int jj, int gg, int buf, bool store) {
     if (w < NBLK) {
       const int qb = w / NDB, db = w % NDB;
       const uint16_t* kt_tile = sK[gg];
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         else dq0 = mfma_k32(ak, bs, dq0);
       }
       const int q = jj * TQ + 16 * qb + c;
-      if (q < N) {
+      if (store && q < N) {
         float* dst = a.dq_partial + (t * part_rows + row0 + gg * ostride + q) * D;
         *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = (dq0 + dq1) * scale;
       }
@@ -327,6 +328,10 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       const int buf = it & 1;
       const uint16_t* tq = sQ[buf];
       const uint16_t* tdo = sdO[buf];
+
+      // dQ of the previous stage (its dS^T tile was completed at the previous barrier);
+      // at the first stage it runs on the idle buffer and stores nothing
+      dq_stage(jp, gp, buf ^ 1, it > 0);
 
       const QT kb = ld_shared<QT>(&sK[gs][Lay<D>::k(16 * w + c, g * QL)]);
 #pragma unroll
@@ -374,9 +379,6 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         }
       }
 
-      // dQ of the previous stage (its dS^T tile was completed at the previous barrier)
-      if (it > 0) dq_stage(jp, gp, buf ^ 1);
-
       if (it + 1 < n_it) {
         stage(buf ^ 1);
         if (gs == nsl - 1) stage_bias((j + 1) & 1);
@@ -418,7 +420,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         }
     }
   }
-  if (n_it > 0) dq_stage(jp, gp, (n_it - 1) & 1);
+  if (n_it > 0) dq_stage(jp, gp, (n_it - 1) & 1, true);
 
   // epilogue: dK = scale * dK^T^T, dV
   if (kok) {
