@@ -37,7 +37,10 @@
  * a pointer not 16-byte aligned TRI_ATTN_ERR_ALIGN, and a failed launch
  * TRI_ATTN_ERR_LAUNCH; in every error case nothing has been enqueued except
  * for TRI_ATTN_ERR_LAUNCH.  Device faults surface at the caller's next
- * synchronisation, as for any HIP call.  NaN and Inf inputs propagate.
+ * synchronisation, as for any HIP call.  NaN and Inf inputs propagate; bias
+ * entries must be finite (the forward adds the bias with an exact identity
+ * matrix product, where an infinite entry also turns the other scores of its
+ * 16 x 16 score block into NaN), so keys are removed through the mask.
  *
  * Determinism: for fixed dimensions and build, every output is bitwise
  * reproducible across calls on the same GPU model.  No float atomics are

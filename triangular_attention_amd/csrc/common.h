@@ -86,6 +86,24 @@ __device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds
                                            0, 0);
 }
 
+// The same direct load issued as inline assembly, invisible to the compiler's
+// wait-count bookkeeping.  The compiler tracks every direct load it knows of as a
+// pending LDS write and waits for it (vmcnt(0)) before any LDS read it cannot prove
+// disjoint, which would serialise a prefetch into one buffer with the reads of the
+// other.  Callers of this form wait for their direct loads themselves (s_waitcnt
+// vmcnt(0) before the barrier that publishes a tile).  The compiler's own counted
+// waits stay correct: a load it tracks cannot complete before the younger loads it
+// also tracks, so untracked loads only make those waits stricter.
+// rsrc: buffer descriptor words (wave-uniform); lds: wave-uniform LDS address (M0).
+__device__ __forceinline__ u32x4 make_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+__device__ __forceinline__ void dma16(u32x4 rsrc, const void* lds, uint32_t off) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(lds);
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(m0), "v"(off), "s"(rsrc) : "memory");
+}
+
 template <typename T> __device__ __forceinline__ T ld_shared(const uint16_t* p) {
   return *reinterpret_cast<const T*>(p);
 }
@@ -148,6 +166,19 @@ __device__ __forceinline__ u32x4 ds_read_tr8_at(const uint16_t* tile, int off_lo
   const u32x2 lo = ds_read_tr(tile + off_lo);
   const u32x2 hi = ds_read_tr(tile + off_hi);
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Workgroup barrier for LDS tiles filled by direct global->LDS loads.
+// __syncthreads() also orders global memory, which makes the compiler wait for
+// every outstanding vector-memory load (register prefetches included) before
+// the barrier.  Here the caller waits for the direct loads explicitly (in-order
+// completion, s_waitcnt vmcnt(n)), this wave's LDS reads are waited for
+// (lgkmcnt(0)), and compiler barriers keep memory accesses on their side.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), other counters unconstrained
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // max over the 4 lane groups that share a column (lanes c, c+16, c+32, c+48)

@@ -7,18 +7,31 @@
 //
 // Work split: one workgroup = one (b, o, h) slice and 128 queries; four waves
 // of 32 queries each.  Scores are computed transposed, S^T = K Q^T, so that a
-// lane owns one query column: the row statistics (max, sum) of a query live
-// in one lane plus its three partner lanes, the bias row of a query is read
-// as contiguous 16-byte chunks, and the bf16 probability block is already the
-// B operand of O^T = V^T P^T.  K and V tiles of 64 keys go from memory
-// straight into LDS (row-major, double-buffered, shared by the four waves);
-// the V^T operand is read with the LDS transposing read.  Bias and mask of the
-// next tile are loaded into registers while the current tile is in flight.
+// lane owns one query column, the bias row of a query is read as contiguous
+// 16-byte chunks, and the bf16 probability block is already the B operand of
+// O^T = V^T P^T; the V^T operand comes from the LDS transposing read.
 //
-// The running maximum is only moved when a tile raises it by more than 8 ln 2:
-// until then the probabilities are taken relative to the old maximum (at most
-// 2^8, exact in FP32 and bf16), and the accumulator rescale is skipped for the
-// whole wave.
+// Data movement: everything a key tile needs (K, V, the 64 mask values and
+// the block's 128 x 64 bias tile) is requested one tile ahead with direct
+// global->LDS loads into double-buffered LDS, so the loop has no register
+// prefetch and one wait (all loads done) plus one barrier per tile.  The
+// memory pipeline, not the ALUs, limits this kernel: per-lane 16-byte loads
+// of mask and bias from every wave cost more address-unit time than the
+// arithmetic, so the per-key mask is loaded once per workgroup.
+//
+// Score arithmetic, kept short:
+//  * bias and mask enter through one exact matrix product per score block:
+//    identity (bf16) times the bias block, accumulated onto the mask;
+//  * the softmax scale is folded into Q once, as a pair of bf16 terms
+//    (hi + lo, relative error about 2^-18), so Q K^T needs no per-score scaling;
+//  * there is no per-tile maximum pass: probabilities are taken relative to
+//    the running reference maximum, and only when a lane's tile sum reaches
+//    2^64 (or at the first tile) is the tile's maximum formed, the
+//    accumulators rescaled and the tile's probabilities recomputed.  FP32 and
+//    bf16 hold values up to 2^64 with unchanged relative precision, and the
+//    common factor cancels in O and in lse.
+// Consequence for the inputs: bias entries must be finite (a 0 * inf in the
+// identity product would spread NaN); masking goes through the mask.
 //
 // Block order: all query tiles of a slice run on one XCD (blocks are dispatched
 // round-robin over 8 XCDs), so K and V of the slice are fetched once into that
@@ -31,20 +44,25 @@
 namespace tri {
 
 template <int D, bool MASK, bool VEC>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
   constexpr int TQ = kFwdQueryTile, TK = kFwdKeyTile;
-  constexpr int KP = D + 8;    // K / V tile pitch (bf16), one row per key
-  constexpr int KCH = KP / 8;  // 16-byte slots per padded row
+  constexpr int KP = D;        // K / V tile pitch (bf16), one row per key, 16-byte chunks swizzled
   constexpr int CH = D / 8;    // 16-byte chunks of data per row
-  constexpr int NKPIECE = TK * KCH / 64;   // whole-wave 1 KB pieces per tile
-  static_assert(TK * KCH % 64 == 0, "K/V tile must be whole wave pieces");
+  constexpr int NKPIECE = TK * CH / 64;    // whole-wave 1 KB pieces per K (or V) tile
+  static_assert(NKPIECE == 2 || NKPIECE == 4, "K/V tiles must split over the four waves");
   constexpr int NDB = D / 16;  // 16-wide feature blocks of O
-  constexpr float kRescale = 5.545177444479562f;   // 8 ln 2: growth that forces a rescale
+  constexpr float kSumLimit = 0x1p64f;     // tile sum that forces a new reference maximum
   typedef typename DOp<D>::T QT;
   constexpr int QL = DOp<D>::kPerLane;
 
-  __shared__ __align__(16) uint16_t sK[2][TK * KP];
-  __shared__ __align__(16) uint16_t sV[2][TK * KP];
+  // separate arrays per buffer: the compiler can then tell the in-flight
+  // direct loads into one buffer from the reads of the other
+  __shared__ __align__(16) uint16_t sK0[TK * KP], sK1[TK * KP];
+  __shared__ __align__(16) uint16_t sV0[TK * KP], sV1[TK * KP];
+  __shared__ __align__(16) float sM0[256], sM1[256];   // mask of the tile (first 64 floats)
+  // bias tile: 128 query rows x 64 keys, 128-byte rows with swizzled 16-byte chunks;
+  // wave w stages (and alone reads) rows 32w .. 32w + 31
+  __shared__ __align__(16) uint16_t sB0[TQ * TK], sB1[TQ * TK];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -69,32 +87,99 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.bias + ((int64_t)b * a.H + h) * N * N, (uint32_t)N * N * 2);
   const __amdgpu_buffer_rsrc_t rM =
       make_rsrc(MASK ? (const void*)(a.mask + (int64_t)bo * N) : (const void*)a.q, MASK ? (uint32_t)N * 4 : 0u);
-  const float scale = a.scale;
 
-  // queries of this lane (rows past N read as zero and are never stored)
+  // queries of this lane (rows past N read as zero and are never stored),
+  // pre-multiplied by the scale and split into hi + lo bf16 terms
   int qrow[2];
   uint32_t boff[2];
-  QT qop[2];
+  QT qhi[2], qlo[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     qrow[qb] = qt * TQ + 32 * w + 16 * qb + c;
     const uint32_t qo = (uint32_t)(qrow[qb] * D + g * QL) * 2;
-    if constexpr (D == 32) qop[qb] = buf_ld16(rQ, qo);
-    else qop[qb] = buf_ld8(rQ, qo);
+    QT q;
+    if constexpr (D == 32) q = buf_ld16(rQ, qo);
+    else q = buf_ld8(rQ, qo);
+#pragma unroll
+    for (int j = 0; j < QL / 2; ++j) {
+      const float x0 = bf_lo(q[j]) * a.scale, x1 = bf_hi(q[j]) * a.scale;
+      const uint32_t hw = pack_bf16(x0, x1);
+      qhi[qb][j] = hw;
+      qlo[qb][j] = pack_bf16(x0 - bf_lo(hw), x1 - bf_hi(hw));
+    }
     boff[qb] = (uint32_t)qrow[qb] * N * 2;
+  }
+
+  // identity block (A operand of the 16x16x16 product): lane (g, c) holds
+  // row c, slots 4g..4g+3
+  u32x2 ident;
+  {
+    const int i = c & 3;
+    const bool mine = (c >> 2) == g;
+    const uint32_t one = (i & 1) ? 0x3F800000u : 0x3F80u;
+    ident[0] = (mine && i < 2) ? one : 0u;
+    ident[1] = (mine && i >= 2) ? one : 0u;
   }
 
   const int nkt = (N + TK - 1) / TK;
   const bool ragged = (N % TK) != 0;
 
-  // K and V tiles: whole-wave pieces, lane l of a piece fills 16-byte slot l of the padded
-  // tile; padding slots reload the row's first chunk, rows past N read as zero
-  auto load_kv = [&](int kt, int buf) {
-    for (int pc = w; pc < 2 * NKPIECE; pc += 4) {
-      const int which = pc / NKPIECE, piece = pc % NKPIECE;
-      const int slot = piece * 64 + lane, row = slot / KCH, ch = slot % KCH;
-      const uint32_t off = (uint32_t)((kt * TK + row) * D + (ch < CH ? ch : 0) * 8) * 2;
-      buf_to_lds16(which ? rV : rK, (which ? sV[buf] : sK[buf]) + piece * 512, off);
+  // Direct global->LDS loads of a tile, in whole-wave pieces (lane l of a piece fills
+  // 16-byte slot l).  K and V tiles are unpadded, with the 16-byte chunks of row r stored
+  // at position chunk ^ sw(r) (the source address of each lane is permuted, so the loads
+  // stay whole-wave): the K operand reads and the transposing V^T reads then spread over
+  // the LDS banks.  With D = 32 each wave loads one K and one V piece, with D = 16 one
+  // piece of K (waves 0, 1) or V (waves 2, 3).  Every wave also loads the tile's 64 mask
+  // values (lanes 0..15; the others, and the whole piece without a mask, read zeros past
+  // the end of the buffer): all waves write the same bytes.  With 16-byte aligned bias
+  // rows (N % 8 == 0) each wave then loads its 32 bias rows of the tile (four pieces,
+  // chunk position chunk ^ swb(row)); otherwise the bias goes through registers.
+  // Tiles beyond N read zeros into the free buffer.  Per-lane offsets are fixed; a tile
+  // only adds its key offset.  Everything a tile reads from LDS was requested one tile
+  // earlier, and the only wait is vmcnt(0) before the barrier that ends each tile.
+  constexpr uint32_t kOOB = 0xFFFFF000u;       // any offset past every buffer
+  constexpr bool LDSIN = VEC;                  // mask and bias through LDS (16-byte aligned rows)
+  constexpr bool MLDS = MASK && LDSIN;
+  auto sw = [](int r) { return (r >> 3) & (CH - 1); };
+  auto swb = [](int r) { return (r >> 1) & 7; };   // bias rows: 8 chunks of 8 keys
+  uint32_t kv_off, m_off, b_off[4];
+  {
+    const int piece = NKPIECE == 4 ? w : (w & 1);
+    const int row = piece * (64 / CH) + lane / CH, pos = lane % CH;
+    kv_off = (uint32_t)(row * D + (pos ^ sw(row)) * 8) * 2;
+    m_off = (MLDS && lane < TK / 4) ? (uint32_t)lane * 16 : kOOB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rl = 8 * j + lane / 8, pos8 = lane % 8;   // row within the wave's 32
+      const int q = qt * TQ + 32 * w + rl;
+      b_off[j] = (uint32_t)q * N * 2 + (uint32_t)((pos8 ^ swb(rl)) * 16);
+    }
+  }
+  // descriptor words for the untracked direct loads (used when every input of the
+  // loop comes through LDS); the tracked form otherwise
+  const u32x4 wK = make_rsrc_words(a.k + slice * D, sbytes), wV = make_rsrc_words(a.v + slice * D, sbytes);
+  const u32x4 wB = make_rsrc_words(a.bias + ((int64_t)b * a.H + h) * N * N, (uint32_t)N * N * 2);
+  const u32x4 wM = make_rsrc_words(MASK ? (const void*)(a.mask + (int64_t)bo * N) : (const void*)a.q,
+                                    MASK ? (uint32_t)N * 4 : 0u);
+  auto ld2lds = [&](const __amdgpu_buffer_rsrc_t& r, const u32x4& rw, void* dst, uint32_t off) {
+    if constexpr (LDSIN) dma16(rw, dst, off);
+    else buf_to_lds16(r, dst, off);
+  };
+  auto load_kv = [&](int kt, uint16_t* dK, uint16_t* dV, float* dM, uint16_t* dB) {
+    const bool real = kt < nkt;
+    const uint32_t kvo = real ? (uint32_t)(kt * TK * D) * 2 + kv_off : kOOB;
+    if constexpr (NKPIECE == 4) {
+      ld2lds(rK, wK, dK + w * 512, kvo);
+      ld2lds(rV, wV, dV + w * 512, kvo);
+    } else {
+      if (w < 2) ld2lds(rK, wK, dK + (w & 1) * 512, kvo);
+      else ld2lds(rV, wV, dV + (w & 1) * 512, kvo);
+    }
+    ld2lds(rM, wM, dM, real && m_off != kOOB ? (uint32_t)(kt * TK) * 4 + m_off : kOOB);
+    if constexpr (LDSIN) {
+      const uint32_t bo = (uint32_t)(kt * TK) * 2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(wB, dB + (32 * w + 8 * j) * TK, real ? bo + b_off[j] : kOOB);
     }
   };
 
@@ -133,114 +218,187 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   };
 
   float mref[2] = {-INFINITY, -INFINITY};   // reference maximum (natural units)
-  float lsum[2] = {0.f, 0.f};
+  float lsum[2] = {0.f, 0.f};               // this lane's part of the row sum, relative to mref
   f32x4 oacc[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one key tile; TAIL = the last tile has keys past N (their scores become -inf)
-  auto tile = [&](int kt, auto tail_tag) {
+  // one key tile; TAIL = the last tile has keys past N (their scores become -inf);
+  // BUF = which LDS buffer holds the tile
+  auto tile = [&](int kt, auto tail_tag, auto buf_tag) {
     constexpr bool TAIL = decltype(tail_tag)::value;
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nkt;
+    constexpr int BUF = decltype(buf_tag)::value;
+    uint16_t* const tK = BUF ? sK1 : sK0;
+    uint16_t* const tV = BUF ? sV1 : sV0;
+    float* const tM = BUF ? sM1 : sM0;
+    uint16_t* const tB = BUF ? sB1 : sB0;
+    if constexpr (LDSIN) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int rl = 16 * qb + c, ch = 4 * m + g;
+          rb[qb][m] = ld_shared<u32x4>(&tB[(32 * w + rl) * TK + ((ch ^ swb(rl)) * 8)]);
+        }
+    }
+    if constexpr (MLDS) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) rm[m][e] = *reinterpret_cast<const f32x4*>(&tM[32 * m + 8 * g + 4 * e]);
+    }
 
     // S^T blocks: rows = keys 32m + 8(r/4) + 4e + (r%4), so that lane group g
-    // holds keys 32m + 8g + 4e + 0..3 (contiguous bias/mask, and the V^T slots)
+    // holds keys 32m + 8g + 4e + 0..3 (contiguous bias/mask, and the V^T slots).
+    // bias + mask first (identity product), then K (scale Q)^T as lo and hi terms.
     f32x4 sacc[2][2][2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int kl = 32 * m + 8 * (c >> 2) + 4 * e + (c & 3);
-        const QT ka = ld_shared<QT>(&sK[cur][kl * KP + g * QL]);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sacc[qb][m][e] = DOp<D>::mma(ka, qop[qb], f32x4{0.f, 0.f, 0.f, 0.f});
-      }
-
-    // scores: s * scale + bias (+ mask)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t wd = rb[qb][m][2 * e + (i >> 1)];
-            const float bv = (i & 1) ? bf_hi(wd) : bf_lo(wd);
-            float x = fmaf(sacc[qb][m][e][i], scale, bv);
-            if (MASK) x += rm[m][e][i];
-            if (TAIL) {
-              const int kx2 = kt * TK + 32 * m + 8 * g + 4 * e + i;
-              x = kx2 < N ? x : -INFINITY;
-            }
-            sacc[qb][m][e][i] = x;
-          }
-    if (more) load_bm(kt + 1);
+          sacc[qb][m][e] = mfma_k16(ident, u32x2{rb[qb][m][2 * e], rb[qb][m][2 * e + 1]},
+                                    MASK ? rm[m][e] : f32x4{0.f, 0.f, 0.f, 0.f});
+    if constexpr (!LDSIN) {
+      if (kt + 1 < nkt) load_bm(kt + 1);
+    }
 
-    u32x4 pp[2][2];
+    QT ka[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int kl = 32 * m + 8 * (c >> 2) + 4 * e + (c & 3);
+        const int kc = (g * QL) / 8;   // 16-byte chunk of this lane's features
+        ka[m][e] = ld_shared<QT>(&tK[kl * KP + ((kc ^ sw(kl)) * 8) + (g * QL) % 8]);
+      }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) sacc[qb][m][e] = DOp<D>::mma(ka[m][e], qlo[qb], sacc[qb][m][e]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) sacc[qb][m][e] = DOp<D>::mma(ka[m][e], qhi[qb], sacc[qb][m][e]);
+
+    if (TAIL) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int kx2 = kt * TK + 32 * m + 8 * g + 4 * e + i;
+              sacc[qb][m][e][i] = kx2 < N ? sacc[qb][m][e][i] : -INFINITY;
+            }
+    }
+
+    // V^T operands of the tile: contraction over the 32 keys of group m
+    u32x4 va[2][NDB];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        // lane (k, a) of its group: rows r0 + k and r0 + 4 + k, columns 16 db + 4a .. +3
+        const int k = (lane & 15) >> 2, a4 = 16 * db + 4 * (lane & 3);
+        const int r0 = 32 * m + 8 * g + k, r1 = r0 + 4;
+        va[m][db] = ds_read_tr8_at(tV, r0 * KP + (((a4 >> 3) ^ sw(r0)) * 8) + (a4 & 7),
+                                   r1 * KP + (((a4 >> 3) ^ sw(r1)) * 8) + (a4 & 7));
+      }
+
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float tmax = -INFINITY;
+      u32x4 pp[2];
+      // probabilities relative to mref, packed to bf16, and their column sums
+      auto probs = [&]() {
+        const float nm = -mref[qb] * kLog2e;
+        float ts = 0.f;
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m) {
+          float p[2][4];
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
+          for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sacc[qb][m][e][i]);
-      tmax = wave_max_groups(tmax);
-      if (__any(tmax > mref[qb] + kRescale)) {
+            for (int i = 0; i < 4; ++i) {
+              p[e][i] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][m][e][i], kLog2e, nm));
+              ts += p[e][i];
+            }
+          pp[m] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
+                        pack_bf16(p[1][2], p[1][3])};
+        }
+        return ts;
+      };
+      // new reference maximum: the tile's maximum (or the old one if larger)
+      auto rebase = [&]() {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sacc[qb][m][e][i]);
+        tmax = wave_max_groups(tmax);
         const float mnew = fmaxf(mref[qb], tmax);
         const float alpha = __builtin_amdgcn_exp2f((mref[qb] - mnew) * kLog2e);
         mref[qb] = mnew;
         lsum[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[db][qb] *= alpha;
+      };
+      float ts;
+      if (kt == 0) {
+        rebase();
+        ts = probs();
+      } else {
+        ts = probs();
+        if (!__all(ts < kSumLimit)) {   // also taken for NaN
+          rebase();
+          ts = probs();
+        }
       }
-      const float nm = -mref[qb] * kLog2e;
+      lsum[qb] += ts;
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        float p[2][4];
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[e][i] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][m][e][i], kLog2e, nm));
-            lsum[qb] += p[e][i];
-          }
-        pp[qb][m] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
-                          pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
-      }
+        for (int db = 0; db < NDB; ++db) oacc[db][qb] = mfma_k32(va[m][db], pp[m], oacc[db][qb]);
     }
 
-    // O^T += V^T P^T: contraction over the 32 keys of group m; V^T by transposing reads
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x4 va = ds_read_tr8<KP>(&sV[cur][(32 * m + 8 * g) * KP + 16 * db], lane);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma_k32(va, pp[qb][m], oacc[db][qb]);
-      }
-
-    // the next tile's direct loads were issued after the previous barrier
+    // the next tile's direct loads (and register loads) were issued one tile ago
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __syncthreads();
-    if (kt + 2 < nkt) load_kv(kt + 2, cur);
+    lds_barrier();
+    load_kv(kt + 2, tK, tV, tM, tB);
   };
 
-  load_kv(0, 0);
-  load_bm(0);
+  load_kv(0, sK0, sV0, sM0, sB0);
+  if constexpr (!LDSIN) load_bm(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  if (nkt > 1) load_kv(1, 1);
+  load_kv(1, sK1, sV1, sM1, sB1);
 
+  using F = std::integral_constant<bool, false>;
+  using T = std::integral_constant<bool, true>;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
   const int nfull = ragged ? nkt - 1 : nkt;
-  for (int kt = 0; kt < nfull; ++kt) tile(kt, std::integral_constant<bool, false>{});
-  if (ragged) tile(nkt - 1, std::integral_constant<bool, true>{});
+  int kt = 0;
+  for (; kt + 2 <= nfull; kt += 2) {
+    tile(kt, F{}, B0{});
+    tile(kt + 1, F{}, B1{});
+  }
+  if (kt < nfull) tile(kt++, F{}, B0{});
+  if (ragged) {
+    if (kt & 1) tile(kt, T{}, B1{});
+    else tile(kt, T{}, B0{});
+  }
 
   // epilogue: O = bf16(O32), E = bf16(O32 - O), lse = m + log l
 #pragma unroll
