@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--workload", default="n768_d32_mask")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-compensate", action="store_true", help="run without the output residual")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=25.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
