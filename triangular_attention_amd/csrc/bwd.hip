@@ -28,18 +28,24 @@
 // there) without per-load bounds checks.  With N % 8 == 0 the Q, dO and bias
 // tiles go from memory straight into LDS.
 //
-// LDS layouts (D = 32): Q, dO and K tiles are unpadded 64-byte rows whose four
-// 16-byte chunks are permuted by an XOR with a row-dependent value, chosen so
-// that both the row reads of the score products (16 rows, one chunk) and the
-// transposing reads (4 rows x 32 bytes per 16 lanes) touch distinct banks.
+// LDS layouts (bank conflicts of each access shape were measured on gfx950
+// with probe kernels replaying the exact lane addresses).  D = 32: Q, dO and K
+// tiles are unpadded 64-byte rows whose four 16-byte chunks are permuted by an
+// XOR with a row-dependent value (Q, dO: row bits 3-4; K: row bits 2-3).  The
+// transposing reads are conflict-free; the score-product row reads of Q, dO
+// and K take two passes.  Swapping the two swizzles removes those conflicts
+// but needs more address registers than the kernel has, and measured slower.
+// The dS^T tile is written 16 bytes per lane and read transposed with a
+// 72-element pitch; the bias tile has 256-byte rows whose 8-byte units are
+// permuted by an XOR with the row's low bits (conflict-free transposing reads).
 #include "common.h"
 #include "kernels.h"
 
 namespace tri {
 
 // Element offset of (row, col) in the LDS tiles.  D = 32: unpadded rows, chunk
-// XOR swizzle; Q/dO use a swizzle of row bits 3-4 (rows 8 apart differ), K of
-// row bits 2-3 (rows 4 apart differ).  D = 16: rows padded to 24 elements.
+// XOR swizzle: Q/dO by row bits 3-4, K by row bits 2-3.  D = 16: rows padded
+// to 24 elements.
 template <int D> struct Lay;
 template <> struct Lay<32> {
   static constexpr int kRowElems = 32;
@@ -70,7 +76,6 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int TQ = kBwdQueryTile, G = kBwdGroup;
   constexpr int RE = Lay<D>::kRowElems;   // LDS elements per Q / dO / K row
   constexpr int SP = TQ + 8;      // dS^T tile pitch (row = key)
-  constexpr int BP = TK + 8;      // bias tile pitch (row = query)
   constexpr int CH = D / 8;       // 16-byte chunks per row in memory
   constexpr int NDB = D / 16;
   constexpr int NQCH = TQ * CH;   // chunks of one Q (or dO) tile
@@ -88,7 +93,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) float sDl[2][TQ];   // -delta
   __shared__ __align__(16) uint16_t sdS[2][TK * SP];
   __shared__ __align__(16) uint16_t sK[G][TK * RE];
-  __shared__ __align__(16) uint16_t sB[2][TQ * BP];
+  __shared__ __align__(16) uint16_t sB[2][TQ * TK];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
@@ -217,16 +222,21 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     }
   };
 
-  // ---- bias tile of (query tile j, key tile t), staged row-major [query][key]
-  constexpr int BCH = BP / 8;                    // 16-byte slots per padded bias row
+  // ---- bias tile of (query tile j, key tile t), staged [query][key]: 256-byte rows,
+  // 8-byte unit u of row r stored at unit position u ^ bsw(r) (bsw even, so 16-byte
+  // chunks stay whole for the direct loads)
+  static_assert(TK == 128, "bias tile layout assumes 128 keys");
+  auto bsw = [](int r) { return ((r & 3) << 2) | (((r >> 3) & 1) << 4); };
+  auto b_at = [&](int r, int key) { return 128 * r + 4 * ((key >> 2) ^ bsw(r)) + (key & 3); };
+  constexpr int BCH = TK / 8;                    // 16-byte slots per bias row
   constexpr int NBPIECE = TQ * BCH / 64;
   static_assert(TQ * BCH % 64 == 0, "bias tile must be whole wave pieces");
   u32x4 rbt[VEC ? 1 : NRB];
   auto load_bias = [&](int j, int bbuf) {
     if (VEC) {
       for (int piece = w; piece < NBPIECE; piece += NW) {
-        const int slot = piece * 64 + lane, row = slot / BCH, ch = slot % BCH;
-        const int q = j * TQ + row, k0 = t * TK + (ch < TK / 8 ? ch : 0) * 8;
+        const int slot = piece * 64 + lane, row = slot / BCH, ch = (slot % BCH) ^ (bsw(row) >> 1);
+        const int q = j * TQ + row, k0 = t * TK + ch * 8;
         // N % 8 == 0: a chunk of 8 keys is entirely in or out of range; out of range
         // chunks (and rows past N) read past the extent and land as zeros
         const uint32_t off = k0 < N ? (uint32_t)(q * N + k0) * 2 : 0xfffffff0u;
@@ -259,7 +269,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         const int ci = tid + r * NT;
         if (ci < NBCH) {
           const int row = ci / (TK / 8), ch = ci % (TK / 8);
-          *reinterpret_cast<u32x4*>(&sB[bbuf][row * BP + ch * 8]) = rbt[r];
+          *reinterpret_cast<u32x4*>(&sB[bbuf][b_at(row, ch * 8)]) = rbt[r];
         }
       }
     }
@@ -317,7 +327,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const int r0 = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);
-      const u32x2 bw = ds_read_tr(&sB[j & 1][(r0 + trk) * BP + 16 * w + 4 * tra]);
+      const u32x2 bw = ds_read_tr(&sB[j & 1][b_at(r0 + trk, 16 * w + 4 * tra)]);
       bb[qb] = f32x4{bf_lo(bw[0]), bf_hi(bw[0]), bf_lo(bw[1]), bf_hi(bw[1])} * kLog2e;
     }
     f32x4 dbacc[4];         // sum over the group's slices of the FP32 dS, in slice order
@@ -363,11 +373,11 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
           }
           pP[e] = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
           pS[e] = u32x2{pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3])};
-          *reinterpret_cast<u32x2*>(&sdS[buf][(16 * w + c) * SP + r0]) = pS[e];
         }
         // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries of this half
         const u32x4 bp = u32x4{pP[0][0], pP[0][1], pP[1][0], pP[1][1]};
         const u32x4 bs = u32x4{pS[0][0], pS[0][1], pS[1][0], pS[1][1]};
+        *reinterpret_cast<u32x4*>(&sdS[buf][(16 * w + c) * SP + 32 * st + 8 * g]) = bs;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int qr = 32 * st + 8 * g + trk, qc = 16 * db + 4 * tra;
