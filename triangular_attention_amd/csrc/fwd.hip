@@ -129,9 +129,8 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
   // at position chunk ^ sw(r) (the source address of each lane is permuted, so the loads
   // stay whole-wave): the K operand reads and the transposing V^T reads then spread over
   // the LDS banks.  With D = 32 each wave loads one K and one V piece, with D = 16 one
-  // piece of K (waves 0, 1) or V (waves 2, 3).  Every wave also loads the tile's 64 mask
-  // values (lanes 0..15; the others, and the whole piece without a mask, read zeros past
-  // the end of the buffer): all waves write the same bytes.  With 16-byte aligned bias
+  // piece of K (waves 0, 1) or V (waves 2, 3).  With a mask, wave 0 also loads the tile's
+  // 64 mask values (lanes 0..15; the others read zeros past the end of the buffer).  With 16-byte aligned bias
   // rows (N % 8 == 0) each wave then loads its 32 bias rows of the tile (four pieces,
   // chunk position chunk ^ swb(row)); otherwise the bias goes through registers.
   // Tiles beyond N read zeros into the free buffer.  Per-lane offsets are fixed; a tile
@@ -175,7 +174,11 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
       if (w < 2) ld2lds(rK, wK, dK + (w & 1) * 512, kvo);
       else ld2lds(rV, wV, dV + (w & 1) * 512, kvo);
     }
-    ld2lds(rM, wM, dM, real && m_off != kOOB ? (uint32_t)(kt * TK) * 4 + m_off : kOOB);
+    // the tile's 64 mask values: one wave, and only when there is a mask (these
+    // loads are untracked, so the per-wave load count may differ)
+    if constexpr (MLDS) {
+      if (w == 0) dma16(wM, dM, real && m_off != kOOB ? (uint32_t)(kt * TK) * 4 + m_off : kOOB);
+    }
     if constexpr (LDSIN) {
       const uint32_t bo = (uint32_t)(kt * TK) * 2;
 #pragma unroll
