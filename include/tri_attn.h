@@ -64,7 +64,7 @@ typedef enum {
   TRI_ATTN_ERR_LAUNCH = 5
 } tri_attn_status;
 
-/* Problem dimensions.  D must be 16 or 32; B, N_o, H, N >= 1; scale finite. */
+/* Problem dimensions.  D must be 16 or 32; B, N_o, H >= 1; 1 <= N <= 32767; scale finite. */
 typedef struct {
   int64_t B, N_o, H, N, D;
   float scale;

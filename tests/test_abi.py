@@ -60,6 +60,7 @@ def test_validation_errors_before_launch(lib):
     assert _fwd(lib, _dims(D=64)) == 3
     assert _fwd(lib, _dims(D=8)) == 3
     assert _fwd(lib, _dims(N=0)) == 2
+    assert _fwd(lib, _dims(N=32768, N_o=1)) == 2     # 4*N*N must fit in 32 bits
     assert _fwd(lib, _dims(B=0)) == 2
     assert _fwd(lib, _dims(scale=float("nan"))) == 2
     assert _fwd(lib, _dims(scale=float("inf"))) == 2

@@ -17,9 +17,10 @@ tri_attn_status check_dims(const tri_attn_dims* d) {
   if (d->B < 1 || d->N_o < 1 || d->H < 1 || d->N < 1 || d->D < 1) return TRI_ATTN_ERR_SHAPE;
   if (!std::isfinite(d->scale)) return TRI_ATTN_ERR_SHAPE;
   if (d->D != 16 && d->D != 32) return TRI_ATTN_ERR_UNSUPPORTED;
-  // 32-bit index limits of the kernels: every per-tensor row count and N*N fit in int32
+  // 32-bit index limits of the kernels: every per-tensor row count fits in int32 and
+  // the byte size of one FP32 N x N plane (4*N*N) fits in uint32
   const int64_t rows = d->B * d->N_o * d->H * d->N;
-  if (d->N > (1 << 15) || rows > (int64_t(1) << 31) / 64 || d->B * d->N_o > kMaxGridZ ||
+  if (d->N > (1 << 15) - 1 || rows > (int64_t(1) << 31) / 64 || d->B * d->N_o > kMaxGridZ ||
       d->H > kMaxGridZ)
     return TRI_ATTN_ERR_SHAPE;
   return TRI_ATTN_OK;

@@ -93,6 +93,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) float sDl[2][TQ];   // -delta
   __shared__ __align__(16) uint16_t sdS[2][TK * SP];
   __shared__ __align__(16) uint16_t sK[G][TK * RE];
+  __shared__ __align__(16) uint16_t sV[G][TK * RE];   // V rows of the key tile (row-read layout)
   __shared__ __align__(16) uint16_t sB[2][TQ * TK];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
@@ -130,14 +131,11 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   const uint32_t rowbytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rbias = make_rsrc(a.bias + ((int64_t)b * H + h) * N * N, (uint32_t)N * N * 2);
 
-  // per-slice V operand (registers), key mask, K tile (LDS), accumulators
-  QT vB[G];
+  // per-slice key mask, K and V tiles (LDS), accumulators
   float mk2[G];
   f32x4 dk_acc[G][NDB], dv_acc[G][NDB];
 #pragma unroll
   for (int gs = 0; gs < G; ++gs) {
-    QT z = {};
-    vB[gs] = z;
     mk2[gs] = -INFINITY;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -147,14 +145,17 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     if (gs < nsl) {
       const int64_t sr = row0 + gs * ostride;
       if (kok) {
-        vB[gs] = ld_global<QT>(a.v + (sr + key) * D + g * QL);
         mk2[gs] = MASK ? a.mask[((int64_t)b * N_o + grp * G + gs) * N + key] * kLog2e : 0.f;
       }
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + sr * D, rowbytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + sr * D, rowbytes);
       for (int ci = tid; ci < TK * CH; ci += NT) {
         const int r = ci / CH, ch = ci % CH;
-        const u32x4 kv = buf_ld16(rk, (uint32_t)((t * TK + r) * D + ch * 8) * 2);
+        const uint32_t off = (uint32_t)((t * TK + r) * D + ch * 8) * 2;
+        const u32x4 kv = buf_ld16(rk, off);
+        const u32x4 vv = buf_ld16(rv, off);
         *reinterpret_cast<u32x4*>(&sK[gs][Lay<D>::k(r, ch * 8)]) = kv;
+        *reinterpret_cast<u32x4*>(&sV[gs][Lay<D>::q(r, ch * 8)]) = vv;
       }
     }
   }
@@ -282,21 +283,27 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       const int qb = w / NDB, db = w % NDB;
       const uint16_t* kt_tile = sK[gg];
       f32x4 dq0 = f32x4{0.f, 0.f, 0.f, 0.f}, dq1 = f32x4{0.f, 0.f, 0.f, 0.f};
+      // all operand reads first, so their LDS latency overlaps
+      u32x4 ak[TK / 32], bs[TK / 32];
 #pragma unroll
       for (int st = 0; st < TK / 32; ++st) {
         const int kr = 32 * st + 8 * g + trk;
         const int kc = 16 * db + 4 * tra;
-        const u32x4 ak = ds_read_tr8_at(kt_tile, Lay<D>::k(kr, kc), Lay<D>::k(kr + 4, kc));
+        ak[st] = ds_read_tr8_at(kt_tile, Lay<D>::k(kr, kc), Lay<D>::k(kr + 4, kc));
         const int so = (32 * st + 8 * g + trk) * SP + 16 * qb + 4 * tra;
-        const u32x4 bs = ds_read_tr8_at(sdS[buf], so, so + 4 * SP);
-        if (st & 1) dq1 = mfma_k32(ak, bs, dq1);
-        else dq0 = mfma_k32(ak, bs, dq0);
+        bs[st] = ds_read_tr8_at(sdS[buf], so, so + 4 * SP);
       }
+#pragma unroll
+      for (int st = 0; st < TK / 32; ++st) {
+        if (st & 1) dq1 = mfma_k32(ak[st], bs[st], dq1);
+        else dq0 = mfma_k32(ak[st], bs[st], dq0);
+      }
+      // buffer store: rows past N fall outside the slice's extent and are dropped
       const int q = jj * TQ + 16 * qb + c;
-      if (store && q < N) {
-        float* dst = a.dq_partial + (t * part_rows + row0 + gg * ostride + q) * D;
-        *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = (dq0 + dq1) * scale;
-      }
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(a.dq_partial + (t * part_rows + row0 + gg * ostride) * D, (uint32_t)N * D * 4);
+      const uint32_t off = store ? (uint32_t)(q * D + 16 * db + 4 * g) * 4 : 0xFFFFF000u;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (dq0 + dq1) * scale), rs, off, 0, 0);
     }
   };
 
@@ -344,6 +351,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       dq_stage(jp, gp, buf ^ 1, it > 0);
 
       const QT kb = ld_shared<QT>(&sK[gs][Lay<D>::k(16 * w + c, g * QL)]);
+      const QT vb = ld_shared<QT>(&sV[gs][Lay<D>::q(16 * w + c, g * QL)]);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         u32x2 pP[2], pS[2];
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
           const f32x4 nl = *reinterpret_cast<const f32x4*>(&sL[buf][r0]);
           const f32x4 nd = *reinterpret_cast<const f32x4*>(&sDl[buf][r0]);
           const f32x4 s = DOp<D>::mma(qa, kb, nl);         // q.k - lse/scale
-          const f32x4 dp = DOp<D>::mma(da, vB[gs], nd);    // dP - delta
+          const f32x4 dp = DOp<D>::mma(da, vb, nd);        // dP - delta
           float p[4], ds[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -420,13 +428,16 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
 
     if (kok) {
       // this group's dbias partial for (query tile j, key tile t)
-      float* dst = a.dbias_partial + (((int64_t)grp * a.B + b) * H + h) * N * N;
+      // buffer stores: rows past N fall outside the (b, h) plane's extent and are dropped
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(a.dbias_partial + (((int64_t)grp * a.B + b) * H + h) * N * N, (uint32_t)N * N * 4);
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int q = j * TQ + 32 * (qb >> 1) + 8 * g + 4 * (qb & 1) + i;
-          if (q < N) dst[(int64_t)q * N + key] = dbacc[qb][i];
+          const uint32_t off = q < N ? (uint32_t)(q * N + key) * 4 : 0xFFFFF000u;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dbacc[qb][i]), rs, off, 0, 0);
         }
     }
   }
