@@ -74,6 +74,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int NW = TK / 16;     // waves; wave w owns keys 16w..16w+15 of the tile
   constexpr int NT = NW * 64;
   constexpr int TQ = kBwdQueryTile, G = kBwdGroup;
+  static_assert(G >= 2 && G % 2 == 0, "the two stage buffers alternate within a query tile");
   constexpr int RE = Lay<D>::kRowElems;   // LDS elements per Q / dO / K row
   constexpr int SP = TQ + 8;      // dS^T tile pitch (row = key)
   constexpr int CH = D / 8;       // 16-byte chunks per row in memory
@@ -119,17 +120,20 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   const int key = t * TK + 16 * w + c;   // key column owned by this lane
   const bool kok = key < N;
 
-  int nsl = N_o - grp * G;
-  if (nsl > G) nsl = G;
+  // Every group runs G stages per query tile.  When N_o is not a multiple of G
+  // the last group's missing slices run as stages whose inputs all read as zero
+  // (zero buffer extents); their dQ, dK and dV are not stored and their score
+  // gradients are not added to the dbias tile.
+  const int nsl = min(G, N_o - grp * G);
   const int nqt = (N + TQ - 1) / TQ;
-  const int n_it = nqt * nsl;
 
   // rows of slice (b, grp*G + gs, h) start at row0 + gs * ostride in the [B, N_o, H, N] row space
   const int64_t row0 = (((int64_t)b * N_o + grp * G) * H + h) * N;
   const int64_t ostride = (int64_t)H * N;
   const int64_t part_rows = (int64_t)a.B * N_o * H * N;    // rows of one dQ partial
   const uint32_t rowbytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t rbias = make_rsrc(a.bias + ((int64_t)b * H + h) * N * N, (uint32_t)N * N * 2);
+  auto srow = [&](int gs) { return row0 + (gs < nsl ? gs : 0) * ostride; };
+  const uint16_t* bias_plane = a.bias + ((int64_t)b * H + h) * N * N;
 
   // per-slice key mask, K and V tiles (LDS), accumulators
   float mk2[G];
@@ -142,44 +146,49 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       dk_acc[gs][db] = f32x4{0.f, 0.f, 0.f, 0.f};
       dv_acc[gs][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (gs < nsl) {
-      const int64_t sr = row0 + gs * ostride;
-      if (kok) {
-        mk2[gs] = MASK ? a.mask[((int64_t)b * N_o + grp * G + gs) * N + key] * kLog2e : 0.f;
-      }
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + sr * D, rowbytes);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + sr * D, rowbytes);
-      for (int ci = tid; ci < TK * CH; ci += NT) {
-        const int r = ci / CH, ch = ci % CH;
-        const uint32_t off = (uint32_t)((t * TK + r) * D + ch * 8) * 2;
-        const u32x4 kv = buf_ld16(rk, off);
-        const u32x4 vv = buf_ld16(rv, off);
-        *reinterpret_cast<u32x4*>(&sK[gs][Lay<D>::k(r, ch * 8)]) = kv;
-        *reinterpret_cast<u32x4*>(&sV[gs][Lay<D>::q(r, ch * 8)]) = vv;
-      }
+    const bool live = gs < nsl;
+    if (live && kok) mk2[gs] = MASK ? a.mask[((int64_t)b * N_o + grp * G + gs) * N + key] * kLog2e : 0.f;
+    const int64_t sr = srow(gs);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + sr * D, live ? rowbytes : 0u);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + sr * D, live ? rowbytes : 0u);
+    for (int ci = tid; ci < TK * CH; ci += NT) {
+      const int r = ci / CH, ch = ci % CH;
+      const uint32_t off = (uint32_t)((t * TK + r) * D + ch * 8) * 2;
+      const u32x4 kv = buf_ld16(rk, off);
+      const u32x4 vv = buf_ld16(rv, off);
+      *reinterpret_cast<u32x4*>(&sK[gs][Lay<D>::k(r, ch * 8)]) = kv;
+      *reinterpret_cast<u32x4*>(&sV[gs][Lay<D>::q(r, ch * 8)]) = vv;
     }
   }
 
   // ---- staging of one (query tile jj, slice gg) stage: Q, dO, -lse/scale, -delta.
+  // The buffer descriptors start at the tile's first row and end at row N, so the
+  // per-lane offsets do not depend on the stage and rows past N read as zero.
   // Direct path (N % 8 == 0): the tile is covered by whole-wave 1 KB pieces; lane l of
   // a piece fills 16-byte LDS slot l, loading the logical chunk that the layout
   // stores there (padding slots of the D = 16 layout reload chunk 0).
   constexpr int SPR = Lay<D>::kSlotsPerRow;
   constexpr int NQPIECE = TQ * SPR / 64;
   static_assert(TQ * SPR % 64 == 0, "Q tile must be whole wave pieces");
+  static_assert(!VEC || 2 * NQPIECE <= NW, "one Q or dO piece per wave");
+  // direct path: wave w < NQPIECE loads Q piece w, the next NQPIECE waves dO pieces
+  const bool qwave = w < 2 * NQPIECE, dowave = w >= NQPIECE;
+  const int qpiece = dowave ? w - NQPIECE : w;
+  uint32_t qoff;
+  {
+    const int slot = qpiece * 64 + lane, row = slot / SPR, ch = Lay<D>::q_src_chunk(row, slot % SPR);
+    qoff = (uint32_t)(row * D + ch * 8) * 2;
+  }
   u32x4 rq[NR];
   f32x4 rls = f32x4{0.f, 0.f, 0.f, 0.f};
   auto load_stage = [&](int jj, int gg, int buf) {
-    const int64_t sr = row0 + gg * ostride;
-    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.q + sr * D, rowbytes);
-    const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.d_o + sr * D, rowbytes);
+    const int64_t sr = srow(gg) + (int64_t)jj * TQ;     // first row of the tile
+    const bool live = gg < nsl;
+    const uint32_t ext = live ? (uint32_t)(N - jj * TQ) * D * 2 : 0u;
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.q + sr * D, ext);
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.d_o + sr * D, ext);
     if (VEC) {
-      for (int pc = w; pc < 2 * NQPIECE; pc += NW) {
-        const int which = pc >= NQPIECE, piece = which ? pc - NQPIECE : pc;
-        const int slot = piece * 64 + lane, row = slot / SPR, ch = Lay<D>::q_src_chunk(row, slot % SPR);
-        const uint32_t off = (uint32_t)((jj * TQ + row) * D + ch * 8) * 2;
-        buf_to_lds16(which ? rO : rQ, (which ? sdO[buf] : sQ[buf]) + piece * 512, off);
-      }
+      if (qwave) buf_to_lds16(dowave ? rO : rQ, (dowave ? sdO[buf] : sQ[buf]) + qpiece * 512, qoff);
     } else {
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
@@ -187,19 +196,27 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         if (ci < 2 * NQCH) {
           const int which = ci / NQCH, cc = ci % NQCH;
           const int row = cc / CH, ch = cc % CH;
-          const uint32_t off = (uint32_t)((jj * TQ + row) * D + ch * 8) * 2;
-          rq[r] = buf_ld16(which ? rO : rQ, off);
+          rq[r] = buf_ld16(which ? rO : rQ, (uint32_t)(row * D + ch * 8) * 2);
         }
       }
     }
-    if (tid < 2 * TQ / 4) {     // 16 chunks of lse, 16 of delta; rows past N read 0
-      const int which = tid / (TQ / 4), q0 = jj * TQ + 4 * (tid % (TQ / 4));
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc((which ? a.delta : a.lse) + sr, (uint32_t)N * 4);
+    // lanes 0..15 fetch 4 lse values each, lanes 16..31 4 delta values (wave 0)
+    if (tid < 2 * TQ / 4) {
+      const uint32_t lext = live ? (uint32_t)(N - jj * TQ) * 4 : 0u;
+      const uint32_t q0 = 4 * (tid % (TQ / 4));
+      // two uniform descriptors, one per lane half (a per-lane choice of descriptor
+      // would need a loop over its distinct values)
+      const __amdgpu_buffer_rsrc_t rsl = make_rsrc(a.lse + sr, lext);
+      const __amdgpu_buffer_rsrc_t rsd = make_rsrc(a.delta + sr, lext);
       if (VEC) {
-        rls = __builtin_bit_cast(f32x4, buf_ld16(rs, (uint32_t)q0 * 4));
+        if (tid < TQ / 4) rls = __builtin_bit_cast(f32x4, buf_ld16(rsl, q0 * 4));
+        else rls = __builtin_bit_cast(f32x4, buf_ld16(rsd, q0 * 4));
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rls[i] = __uint_as_float(buf_ld4(rs, (uint32_t)(q0 + i) * 4));
+        for (int i = 0; i < 4; ++i) {
+          if (tid < TQ / 4) rls[i] = __uint_as_float(buf_ld4(rsl, (q0 + i) * 4));
+          else rls[i] = __uint_as_float(buf_ld4(rsd, (q0 + i) * 4));
+        }
       }
     }
   };
@@ -232,30 +249,36 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int BCH = TK / 8;                    // 16-byte slots per bias row
   constexpr int NBPIECE = TQ * BCH / 64;
   static_assert(TQ * BCH % 64 == 0, "bias tile must be whole wave pieces");
+  static_assert(!VEC || NBPIECE == 2 * NW, "two bias pieces per wave");
+  // direct path: wave w loads bias pieces w and w + NW; chunks of keys past N get an
+  // offset past every extent and land as zeros (N % 8 == 0: a chunk is entirely in or out)
+  uint32_t boff[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int slot = (w + k * NW) * 64 + lane, row = slot / BCH, ch = (slot % BCH) ^ (bsw(row) >> 1);
+    const int k0 = t * TK + ch * 8;
+    boff[k] = k0 < N ? (uint32_t)(row * N + k0) * 2 : 0xfffffff0u;
+  }
   u32x4 rbt[VEC ? 1 : NRB];
   auto load_bias = [&](int j, int bbuf) {
+    // descriptor from row j*TQ to row N of the (b, h) bias plane
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias_plane + (int64_t)j * TQ * N, (uint32_t)(N - j * TQ) * N * 2);
     if (VEC) {
-      for (int piece = w; piece < NBPIECE; piece += NW) {
-        const int slot = piece * 64 + lane, row = slot / BCH, ch = (slot % BCH) ^ (bsw(row) >> 1);
-        const int q = j * TQ + row, k0 = t * TK + ch * 8;
-        // N % 8 == 0: a chunk of 8 keys is entirely in or out of range; out of range
-        // chunks (and rows past N) read past the extent and land as zeros
-        const uint32_t off = k0 < N ? (uint32_t)(q * N + k0) * 2 : 0xfffffff0u;
-        buf_to_lds16(rbias, sB[bbuf] + piece * 512, off);
-      }
+      buf_to_lds16(rb, sB[bbuf] + w * 512, boff[0]);
+      buf_to_lds16(rb, sB[bbuf] + (w + NW) * 512, boff[1]);
     } else {
 #pragma unroll
       for (int r = 0; r < NRB; ++r) {
         const int ci = tid + r * NT;
         if (ci < NBCH) {
           const int row = ci / (TK / 8), ch = ci % (TK / 8);
-          const int q = j * TQ + row, k0 = t * TK + ch * 8;
+          const int k0 = t * TK + ch * 8;
           uint32_t wv[4];
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
             const int k_lo = k0 + 2 * p;
-            const uint32_t lo = k_lo < N ? buf_ld2(rbias, (uint32_t)(q * N + k_lo) * 2) : 0u;
-            const uint32_t hi = k_lo + 1 < N ? buf_ld2(rbias, (uint32_t)(q * N + k_lo + 1) * 2) : 0u;
+            const uint32_t lo = k_lo < N ? buf_ld2(rb, (uint32_t)(row * N + k_lo) * 2) : 0u;
+            const uint32_t hi = k_lo + 1 < N ? buf_ld2(rb, (uint32_t)(row * N + k_lo + 1) * 2) : 0u;
             wv[p] = lo | (hi << 16);
           }
           rbt[r] = u32x4{wv[0], wv[1], wv[2], wv[3]};
@@ -277,7 +300,8 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   };
 
   // ---- dQ^T block (queries 16qb.., features 16db..) = K^T dS^T over the TK keys of a stage;
-  // wave w computes block w
+  // wave w computes block w.  The partial's descriptor starts at the tile's first row and
+  // ends at row N (extent zero when nothing is to be stored), so rows past N are dropped.
   auto dq_stage = [&](int jj, int gg, int buf, bool store) {
     if (w < NBLK) {
       const int qb = w / NDB, db = w % NDB;
@@ -298,36 +322,32 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         if (st & 1) dq1 = mfma_k32(ak[st], bs[st], dq1);
         else dq0 = mfma_k32(ak[st], bs[st], dq0);
       }
-      // buffer store: rows past N fall outside the slice's extent and are dropped
-      const int q = jj * TQ + 16 * qb + c;
-      const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(a.dq_partial + (t * part_rows + row0 + gg * ostride) * D, (uint32_t)N * D * 4);
-      const uint32_t off = store ? (uint32_t)(q * D + 16 * db + 4 * g) * 4 : 0xFFFFF000u;
+      const int64_t prow = t * part_rows + srow(gg) + (int64_t)jj * TQ;
+      const uint32_t ext = __builtin_amdgcn_readfirstlane(store && gg < nsl ? (uint32_t)(N - jj * TQ) * D * 4 : 0u);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dq_partial + prow * D, ext);
+      const uint32_t off = (uint32_t)((16 * qb + c) * D + 16 * db + 4 * g) * 4;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (dq0 + dq1) * scale), rs, off, 0, 0);
     }
   };
 
-  // register path: regs hold stage it+1 while stage it computes; direct path:
-  // stage it+2 is loaded straight into the LDS buffer that stage it releases
-  if (n_it > 0) {
-    load_stage(0, 0, 0);
-    load_bias(0, 0);
-    stage(0);
-    stage_bias(0);
-    if (!VEC) {
-      if (n_it > 1) load_stage(nsl > 1 ? 0 : 1, nsl > 1 ? 1 : 0, 1);
-      if (nqt > 1) load_bias(1, 1);
-    }
+  // Stage s = (query tile j, slice gs) uses buffer gs & 1.  Register path: regs hold
+  // stage s+1 while stage s computes; direct path: stage s+2 is loaded straight into
+  // the LDS buffer that stage s releases.
+  load_stage(0, 0, 0);
+  load_bias(0, 0);
+  stage(0);
+  stage_bias(0);
+  if (!VEC) {
+    load_stage(0, 1, 1);
+    if (nqt > 1) load_bias(1, 1);
   }
   __syncthreads();
-  if (VEC) {
-    if (n_it > 1) load_stage(nsl > 1 ? 0 : 1, nsl > 1 ? 1 : 0, 1);
-    if (nqt > 1 && nsl == 1) load_bias(1, 1);
-  }
+  if (VEC) load_stage(0, 1, 1);
 
-  int it = 0;
-  int jp = 0, gp = 0;       // the previous stage (its dQ product is still pending)
-  for (int j = 0; j < nqt; ++j) {
+  // one query tile: its G stages and its dbias tile.  FULL: all G slices of the group
+  // exist (every group but a ragged last one), so every stage's dS enters the dbias tile.
+  auto query_tile = [&](int j, auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
     // bias * log2(e) of the lane's (query, key) pairs: one transposing read per block
     // gives rows 32s + 8g + 4e + 0..3 of block qb = 2s + e at the lane's key column
     f32x4 bb[4];
@@ -341,14 +361,15 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
 
 #pragma unroll
     for (int gs = 0; gs < G; ++gs) {
-      if (gs >= nsl) break;
-      const int buf = it & 1;
+      const int buf = gs & 1;
       const uint16_t* tq = sQ[buf];
       const uint16_t* tdo = sdO[buf];
 
-      // dQ of the previous stage (its dS^T tile was completed at the previous barrier);
-      // at the first stage it runs on the idle buffer and stores nothing
-      dq_stage(jp, gp, buf ^ 1, it > 0);
+      // dQ of the previous stage, (j, gs-1) or (j-1, G-1), whose dS^T tile was completed
+      // at the previous barrier; before the first stage it runs on the idle buffer and
+      // stores nothing
+      if (gs > 0) dq_stage(j, gs - 1, buf ^ 1, true);
+      else dq_stage(j > 0 ? j - 1 : 0, G - 1, buf ^ 1, j > 0);
 
       const QT kb = ld_shared<QT>(&sK[gs][Lay<D>::k(16 * w + c, g * QL)]);
       const QT vb = ld_shared<QT>(&sV[gs][Lay<D>::q(16 * w + c, g * QL)]);
@@ -376,7 +397,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
           }
           if (gs == 0) {
             dbacc[qb] = f32x4{ds[0], ds[1], ds[2], ds[3]};
-          } else {
+          } else if (FULL || gs < nsl) {
             dbacc[qb] += f32x4{ds[0], ds[1], ds[2], ds[3]};
           }
           pP[e] = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
@@ -397,51 +418,61 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         }
       }
 
-      if (it + 1 < n_it) {
-        stage(buf ^ 1);
-        if (gs == nsl - 1) stage_bias((j + 1) & 1);
+      if (gs + 1 < G || j + 1 < nqt) {
+        stage(buf ^ 1);       // register-held parts of the next stage (all of it on the register path)
+        if (gs == G - 1) stage_bias((j + 1) & 1);
       }
       // the direct LDS loads of the next stage were issued by this wave after the
       // previous barrier; they must land before any wave reads them
       if (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
       __syncthreads();          // this stage's dS^T complete; next stage's tiles visible
 
-      // stage it+2, two steps ahead in (query tile, slice) order
-      const bool last1 = gs + 1 >= nsl;
-      const int g1 = last1 ? 0 : gs + 1, j1 = last1 ? j + 1 : j;
-      const bool last2 = g1 + 1 >= nsl;
-      const int g2 = last2 ? 0 : g1 + 1, j2 = last2 ? j1 + 1 : j1;
+      // the stage two ahead: (j, gs + 2) or (j + 1, gs + 2 - G)
+      const int j2 = gs + 2 < G ? j : j + 1, g2 = gs + 2 < G ? gs + 2 : gs + 2 - G;
       if (VEC) {
-        // stage it+2 goes into the buffer stage it just released; the bias of tile
-        // j+1 (needed after the last stage of tile j) is fetched one stage ahead
-        if (it + 2 < n_it) load_stage(j2, g2, buf);
-        if (j + 1 < nqt && nsl >= 2 && gs == nsl - 2) load_bias(j + 1, (j + 1) & 1);
-        if (nsl == 1 && j + 2 < nqt) load_bias(j + 2, j & 1);
+        // it goes into the buffer this stage released; the bias of tile j+1 (needed
+        // after the last stage of tile j) is fetched one stage ahead
+        if (j2 < nqt) load_stage(j2, g2, buf);
+        if (gs == G - 2 && j + 1 < nqt) load_bias(j + 1, (j + 1) & 1);
       } else {
-        if (it + 2 < n_it) load_stage(j2, g2, 0);
-        if (gs == nsl - 1 && j + 2 < nqt) load_bias(j + 2, 0);
+        if (j2 < nqt) load_stage(j2, g2, 0);
+        if (gs == G - 1 && j + 2 < nqt) load_bias(j + 2, 0);
       }
-      jp = j;
-      gp = gs;
-      ++it;
     }
 
     if (kok) {
-      // this group's dbias partial for (query tile j, key tile t)
-      // buffer stores: rows past N fall outside the (b, h) plane's extent and are dropped
+      // this group's dbias partial for (query tile j, key tile t); in the last query
+      // tile rows past N go to an offset past the plane's extent and are dropped
       const __amdgpu_buffer_rsrc_t rs =
           make_rsrc(a.dbias_partial + (((int64_t)grp * a.B + b) * H + h) * N * N, (uint32_t)N * N * 4);
+      if ((j + 1) * TQ <= N) {
+        const uint32_t lane_off = (uint32_t)(8 * g * N + key) * 4;
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
+        for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int q = j * TQ + 32 * (qb >> 1) + 8 * g + 4 * (qb & 1) + i;
-          const uint32_t off = q < N ? (uint32_t)(q * N + key) * 4 : 0xFFFFF000u;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dbacc[qb][i]), rs, off, 0, 0);
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int r = j * TQ + 32 * (qb >> 1) + 4 * (qb & 1) + i;   // row of group g = 0
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dbacc[qb][i]), rs, lane_off,
+                                                  (int)((uint32_t)r * N * 4), 0);
+          }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int q = j * TQ + 32 * (qb >> 1) + 8 * g + 4 * (qb & 1) + i;
+            const uint32_t off = q < N ? (uint32_t)(q * N + key) * 4 : 0xFFFFF000u;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dbacc[qb][i]), rs, off, 0, 0);
+          }
+      }
     }
+  };
+  if (nsl == G) {
+    for (int j = 0; j < nqt; ++j) query_tile(j, std::true_type{});
+  } else {
+    for (int j = 0; j < nqt; ++j) query_tile(j, std::false_type{});
   }
-  if (n_it > 0) dq_stage(jp, gp, (n_it - 1) & 1, true);
+  dq_stage(nqt - 1, G - 1, (G - 1) & 1, true);
 
   // epilogue: dK = scale * dK^T^T, dV
   if (kok) {
