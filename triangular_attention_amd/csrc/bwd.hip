@@ -74,7 +74,9 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int NW = TK / 16;     // waves; wave w owns keys 16w..16w+15 of the tile
   constexpr int NT = NW * 64;
   constexpr int TQ = kBwdQueryTile, G = kBwdGroup;
-  static_assert(G >= 2 && G % 2 == 0, "the two stage buffers alternate within a query tile");
+  static_assert(G >= 2 && G % 2 == 0, "stage parity must repeat with every query tile");
+  constexpr int NB = VEC ? 3 : 2;  // Q / dO / -lse / -delta stage buffers
+  constexpr int HW = NW / 2;      // waves per loader set (direct path)
   constexpr int RE = Lay<D>::kRowElems;   // LDS elements per Q / dO / K row
   constexpr int SP = TQ + 8;      // dS^T tile pitch (row = key)
   constexpr int CH = D / 8;       // 16-byte chunks per row in memory
@@ -88,10 +90,10 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   typedef typename DOp<D>::T QT;
   constexpr int QL = DOp<D>::kPerLane;
 
-  __shared__ __align__(16) uint16_t sQ[2][TQ * RE];
-  __shared__ __align__(16) uint16_t sdO[2][TQ * RE];
-  __shared__ __align__(16) float sL[2][TQ];    // -lse / scale of the stage's rows
-  __shared__ __align__(16) float sDl[2][TQ];   // -delta
+  __shared__ __align__(16) uint16_t sQ[NB][TQ * RE];
+  __shared__ __align__(16) uint16_t sdO[NB][TQ * RE];
+  __shared__ __align__(16) float sL[NB][TQ];    // -lse / scale of the stage's rows
+  __shared__ __align__(16) float sDl[NB][TQ];   // -delta
   __shared__ __align__(16) uint16_t sdS[2][TK * SP];
   __shared__ __align__(16) uint16_t sK[G][TK * RE];
   __shared__ __align__(16) uint16_t sV[G][TK * RE];   // V rows of the key tile (row-read layout)
@@ -126,6 +128,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   // gradients are not added to the dbias tile.
   const int nsl = min(G, N_o - grp * G);
   const int nqt = (N + TQ - 1) / TQ;
+  const int nst = G * nqt;        // stages
 
   // rows of slice (b, grp*G + gs, h) start at row0 + gs * ostride in the [B, N_o, H, N] row space
   const int64_t row0 = (((int64_t)b * N_o + grp * G) * H + h) * N;
@@ -164,80 +167,97 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   // ---- staging of one (query tile jj, slice gg) stage: Q, dO, -lse/scale, -delta.
   // The buffer descriptors start at the tile's first row and end at row N, so the
   // per-lane offsets do not depend on the stage and rows past N read as zero.
-  // Direct path (N % 8 == 0): the tile is covered by whole-wave 1 KB pieces; lane l of
-  // a piece fills 16-byte LDS slot l, loading the logical chunk that the layout
-  // stores there (padding slots of the D = 16 layout reload chunk 0).
+  //
+  // Direct path (N % 8 == 0): stage s goes from memory straight into LDS buffer s % 3.
+  // The waves form two loader sets (waves 0..NW/2-1 and NW/2..NW-1); set s % 2 loads
+  // stage s right after the barrier that ends stage s - 3 and waits for it (vmcnt(0))
+  // only at the end of stage s - 1, so every load has two stages of compute to land,
+  // and each wave waits on its memory operations at every other barrier only.  Wave
+  // ws < NQPIECE of a set fills Q piece ws and dO piece ws: lane l of a piece fills
+  // 16-byte LDS slot l with the logical chunk that the layout stores there (padding
+  // slots of the D = 16 layout reload chunk 0).
+  // Register path: regs hold stage s+1 while stage s computes; buffers alternate.
   constexpr int SPR = Lay<D>::kSlotsPerRow;
   constexpr int NQPIECE = TQ * SPR / 64;
   static_assert(TQ * SPR % 64 == 0, "Q tile must be whole wave pieces");
-  static_assert(!VEC || 2 * NQPIECE <= NW, "one Q or dO piece per wave");
-  // direct path: wave w < NQPIECE loads Q piece w, the next NQPIECE waves dO pieces
-  const bool qwave = w < 2 * NQPIECE, dowave = w >= NQPIECE;
-  const int qpiece = dowave ? w - NQPIECE : w;
+  static_assert(!VEC || NQPIECE <= HW, "one Q and one dO piece per wave of a loader set");
+  const int lset = w / HW, ws = w % HW;     // loader set of the wave, wave index within it
   uint32_t qoff;
   {
-    const int slot = qpiece * 64 + lane, row = slot / SPR, ch = Lay<D>::q_src_chunk(row, slot % SPR);
+    const int slot = ws * 64 + lane, row = slot / SPR, ch = Lay<D>::q_src_chunk(row, slot % SPR);
     qoff = (uint32_t)(row * D + ch * 8) * 2;
   }
-  u32x4 rq[NR];
+  // -lse/scale and -delta of a stage: lanes 0..15 fetch 4 lse values each, lanes
+  // 16..31 4 delta values (direct path: first wave of the loading set; register path: wave 0)
+  const bool rls_lane = (VEC ? ws == 0 : w == 0) && lane < 2 * TQ / 4;
+  u32x4 rq[VEC ? 1 : NR];
   f32x4 rls = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto load_stage = [&](int jj, int gg, int buf) {
-    const int64_t sr = srow(gg) + (int64_t)jj * TQ;     // first row of the tile
-    const bool live = gg < nsl;
-    const uint32_t ext = live ? (uint32_t)(N - jj * TQ) * D * 2 : 0u;
-    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.q + sr * D, ext);
-    const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.d_o + sr * D, ext);
-    if (VEC) {
-      if (qwave) buf_to_lds16(dowave ? rO : rQ, (dowave ? sdO[buf] : sQ[buf]) + qpiece * 512, qoff);
-    } else {
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int ci = tid + r * NT;
-        if (ci < 2 * NQCH) {
-          const int which = ci / NQCH, cc = ci % NQCH;
-          const int row = cc / CH, ch = cc % CH;
-          rq[r] = buf_ld16(which ? rO : rQ, (uint32_t)(row * D + ch * 8) * 2);
-        }
-      }
-    }
-    // lanes 0..15 fetch 4 lse values each, lanes 16..31 4 delta values (wave 0)
-    if (tid < 2 * TQ / 4) {
+  auto load_rls = [&](int64_t sr, int jj, bool live) {
+    if (rls_lane) {
       const uint32_t lext = live ? (uint32_t)(N - jj * TQ) * 4 : 0u;
-      const uint32_t q0 = 4 * (tid % (TQ / 4));
+      const uint32_t q0 = 4 * (lane % (TQ / 4));
       // two uniform descriptors, one per lane half (a per-lane choice of descriptor
       // would need a loop over its distinct values)
       const __amdgpu_buffer_rsrc_t rsl = make_rsrc(a.lse + sr, lext);
       const __amdgpu_buffer_rsrc_t rsd = make_rsrc(a.delta + sr, lext);
       if (VEC) {
-        if (tid < TQ / 4) rls = __builtin_bit_cast(f32x4, buf_ld16(rsl, q0 * 4));
+        if (lane < TQ / 4) rls = __builtin_bit_cast(f32x4, buf_ld16(rsl, q0 * 4));
         else rls = __builtin_bit_cast(f32x4, buf_ld16(rsd, q0 * 4));
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (tid < TQ / 4) rls[i] = __uint_as_float(buf_ld4(rsl, (q0 + i) * 4));
+          if (lane < TQ / 4) rls[i] = __uint_as_float(buf_ld4(rsl, (q0 + i) * 4));
           else rls[i] = __uint_as_float(buf_ld4(rsd, (q0 + i) * 4));
         }
       }
     }
   };
-  auto stage = [&](int buf) {
-    if (!VEC) {
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int ci = tid + r * NT;
-        if (ci < 2 * NQCH) {
-          const int which = ci / NQCH, cc = ci % NQCH;
-          const int row = cc / CH, ch = cc % CH;
-          uint16_t* dst = which ? sdO[buf] : sQ[buf];
-          *reinterpret_cast<u32x4*>(&dst[Lay<D>::q(row, ch * 8)]) = rq[r];
-        }
-      }
-    }
-    if (tid < 2 * TQ / 4) {
-      const int which = tid / (TQ / 4), q0 = 4 * (tid % (TQ / 4));
-      if (which) *reinterpret_cast<f32x4*>(&sDl[buf][q0]) = -rls;
+  auto write_rls = [&](int buf) {
+    if (rls_lane) {
+      const int q0 = 4 * (lane % (TQ / 4));
+      if (lane >= TQ / 4) *reinterpret_cast<f32x4*>(&sDl[buf][q0]) = -rls;
       else *reinterpret_cast<f32x4*>(&sL[buf][q0]) = rls * (-1.0f / scale);
     }
+  };
+  auto load_stage_direct = [&](int jj, int gg, int buf) {
+    const int64_t sr = srow(gg) + (int64_t)jj * TQ;     // first row of the tile
+    const bool live = gg < nsl;
+    const uint32_t ext = live ? (uint32_t)(N - jj * TQ) * D * 2 : 0u;
+    if (ws < NQPIECE) {
+      dma16(make_rsrc_words(a.q + sr * D, ext), sQ[buf] + ws * 512, qoff);
+      dma16(make_rsrc_words(a.d_o + sr * D, ext), sdO[buf] + ws * 512, qoff);
+    }
+    load_rls(sr, jj, live);
+  };
+  auto load_stage_regs = [&](int jj, int gg) {
+    const int64_t sr = srow(gg) + (int64_t)jj * TQ;
+    const bool live = gg < nsl;
+    const uint32_t ext = live ? (uint32_t)(N - jj * TQ) * D * 2 : 0u;
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.q + sr * D, ext);
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.d_o + sr * D, ext);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int ci = tid + r * NT;
+      if (ci < 2 * NQCH) {
+        const int which = ci / NQCH, cc = ci % NQCH;
+        const int row = cc / CH, ch = cc % CH;
+        rq[r] = buf_ld16(which ? rO : rQ, (uint32_t)(row * D + ch * 8) * 2);
+      }
+    }
+    load_rls(sr, jj, live);
+  };
+  auto stage_regs = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int ci = tid + r * NT;
+      if (ci < 2 * NQCH) {
+        const int which = ci / NQCH, cc = ci % NQCH;
+        const int row = cc / CH, ch = cc % CH;
+        uint16_t* dst = which ? sdO[buf] : sQ[buf];
+        *reinterpret_cast<u32x4*>(&dst[Lay<D>::q(row, ch * 8)]) = rq[r];
+      }
+    }
+    write_rls(buf);
   };
 
   // ---- bias tile of (query tile j, key tile t), staged [query][key]: 256-byte rows,
@@ -249,52 +269,51 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int BCH = TK / 8;                    // 16-byte slots per bias row
   constexpr int NBPIECE = TQ * BCH / 64;
   static_assert(TQ * BCH % 64 == 0, "bias tile must be whole wave pieces");
-  static_assert(!VEC || NBPIECE == 2 * NW, "two bias pieces per wave");
-  // direct path: wave w loads bias pieces w and w + NW; chunks of keys past N get an
+  static_assert(!VEC || NBPIECE == 4 * HW, "four bias pieces per wave of loader set 0");
+  // direct path: the bias of a tile is loaded by set 0 (a tile starts at an even
+  // stage); its wave ws loads pieces ws + k * NW/2.  Chunks of keys past N get an
   // offset past every extent and land as zeros (N % 8 == 0: a chunk is entirely in or out)
-  uint32_t boff[2];
+  uint32_t boff[4];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int slot = (w + k * NW) * 64 + lane, row = slot / BCH, ch = (slot % BCH) ^ (bsw(row) >> 1);
+  for (int k = 0; k < 4; ++k) {
+    const int slot = (ws + k * HW) * 64 + lane, row = slot / BCH, ch = (slot % BCH) ^ (bsw(row) >> 1);
     const int k0 = t * TK + ch * 8;
     boff[k] = k0 < N ? (uint32_t)(row * N + k0) * 2 : 0xfffffff0u;
   }
-  u32x4 rbt[VEC ? 1 : NRB];
-  auto load_bias = [&](int j, int bbuf) {
+  auto load_bias_direct = [&](int j, int bbuf) {
     // descriptor from row j*TQ to row N of the (b, h) bias plane
+    const u32x4 rw = make_rsrc_words(bias_plane + (int64_t)j * TQ * N, (uint32_t)(N - j * TQ) * N * 2);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dma16(rw, sB[bbuf] + (ws + k * HW) * 512, boff[k]);
+  };
+  u32x4 rbt[VEC ? 1 : NRB];
+  auto load_bias_regs = [&](int j) {
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias_plane + (int64_t)j * TQ * N, (uint32_t)(N - j * TQ) * N * 2);
-    if (VEC) {
-      buf_to_lds16(rb, sB[bbuf] + w * 512, boff[0]);
-      buf_to_lds16(rb, sB[bbuf] + (w + NW) * 512, boff[1]);
-    } else {
 #pragma unroll
-      for (int r = 0; r < NRB; ++r) {
-        const int ci = tid + r * NT;
-        if (ci < NBCH) {
-          const int row = ci / (TK / 8), ch = ci % (TK / 8);
-          const int k0 = t * TK + ch * 8;
-          uint32_t wv[4];
+    for (int r = 0; r < NRB; ++r) {
+      const int ci = tid + r * NT;
+      if (ci < NBCH) {
+        const int row = ci / (TK / 8), ch = ci % (TK / 8);
+        const int k0 = t * TK + ch * 8;
+        uint32_t wv[4];
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int k_lo = k0 + 2 * p;
-            const uint32_t lo = k_lo < N ? buf_ld2(rb, (uint32_t)(row * N + k_lo) * 2) : 0u;
-            const uint32_t hi = k_lo + 1 < N ? buf_ld2(rb, (uint32_t)(row * N + k_lo + 1) * 2) : 0u;
-            wv[p] = lo | (hi << 16);
-          }
-          rbt[r] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        for (int p = 0; p < 4; ++p) {
+          const int k_lo = k0 + 2 * p;
+          const uint32_t lo = k_lo < N ? buf_ld2(rb, (uint32_t)(row * N + k_lo) * 2) : 0u;
+          const uint32_t hi = k_lo + 1 < N ? buf_ld2(rb, (uint32_t)(row * N + k_lo + 1) * 2) : 0u;
+          wv[p] = lo | (hi << 16);
         }
+        rbt[r] = u32x4{wv[0], wv[1], wv[2], wv[3]};
       }
     }
   };
-  auto stage_bias = [&](int bbuf) {
-    if (!VEC) {
+  auto stage_bias_regs = [&](int bbuf) {
 #pragma unroll
-      for (int r = 0; r < NRB; ++r) {
-        const int ci = tid + r * NT;
-        if (ci < NBCH) {
-          const int row = ci / (TK / 8), ch = ci % (TK / 8);
-          *reinterpret_cast<u32x4*>(&sB[bbuf][b_at(row, ch * 8)]) = rbt[r];
-        }
+    for (int r = 0; r < NRB; ++r) {
+      const int ci = tid + r * NT;
+      if (ci < NBCH) {
+        const int row = ci / (TK / 8), ch = ci % (TK / 8);
+        *reinterpret_cast<u32x4*>(&sB[bbuf][b_at(row, ch * 8)]) = rbt[r];
       }
     }
   };
@@ -330,24 +349,35 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     }
   };
 
-  // Stage s = (query tile j, slice gs) uses buffer gs & 1.  Register path: regs hold
-  // stage s+1 while stage s computes; direct path: stage s+2 is loaded straight into
-  // the LDS buffer that stage s releases.
-  load_stage(0, 0, 0);
-  load_bias(0, 0);
-  stage(0);
-  stage_bias(0);
-  if (!VEC) {
-    load_stage(0, 1, 1);
-    if (nqt > 1) load_bias(1, 1);
+  // ---- prologue: the first stages and the first bias tile
+  if (VEC) {
+    if (lset == 0) {
+      load_stage_direct(0, 0, 0);
+      load_bias_direct(0, 0);
+    } else {
+      load_stage_direct(0, 1, 1);      // G >= 2: stage 1 is slice 1 of query tile 0
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    write_rls(lset);
+    __syncthreads();                   // also publishes the K and V tiles
+    if (lset == 0 && 2 < nst) load_stage_direct(2 / G, 2 % G, 2);
+  } else {
+    load_stage_regs(0, 0);
+    load_bias_regs(0);
+    stage_regs(0);
+    stage_bias_regs(0);
+    load_stage_regs(0, 1);
+    if (nqt > 1) load_bias_regs(1);
+    __syncthreads();
   }
-  __syncthreads();
-  if (VEC) load_stage(0, 1, 1);
 
   // one query tile: its G stages and its dbias tile.  FULL: all G slices of the group
   // exist (every group but a ragged last one), so every stage's dS enters the dbias tile.
-  auto query_tile = [&](int j, auto full_c) {
+  // R0: position of the tile's first stage in the 3-tile cycle of direct-path buffers
+  // (stage s uses buffer s % 3; tiles come in triples, so R0 is 0, G or 2G).
+  auto query_tile = [&](int j, auto full_c, auto r0_c) {
     constexpr bool FULL = decltype(full_c)::value;
+    constexpr int R0 = decltype(r0_c)::value;
     // bias * log2(e) of the lane's (query, key) pairs: one transposing read per block
     // gives rows 32s + 8g + 4e + 0..3 of block qb = 2s + e at the lane's key column
     f32x4 bb[4];
@@ -361,15 +391,18 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
 
 #pragma unroll
     for (int gs = 0; gs < G; ++gs) {
-      const int buf = gs & 1;
+      const int r = R0 + gs;                 // stage index modulo 3 * G
+      const int s = G * j + gs;              // stage index
+      const int buf = VEC ? r % 3 : gs & 1;  // Q / dO / -lse / -delta buffer
+      const int dsb = gs & 1;                // dS^T buffer
       const uint16_t* tq = sQ[buf];
       const uint16_t* tdo = sdO[buf];
 
       // dQ of the previous stage, (j, gs-1) or (j-1, G-1), whose dS^T tile was completed
       // at the previous barrier; before the first stage it runs on the idle buffer and
       // stores nothing
-      if (gs > 0) dq_stage(j, gs - 1, buf ^ 1, true);
-      else dq_stage(j > 0 ? j - 1 : 0, G - 1, buf ^ 1, j > 0);
+      if (gs > 0) dq_stage(j, gs - 1, dsb ^ 1, true);
+      else dq_stage(j > 0 ? j - 1 : 0, G - 1, dsb ^ 1, j > 0);
 
       const QT kb = ld_shared<QT>(&sK[gs][Lay<D>::k(16 * w + c, g * QL)]);
       const QT vb = ld_shared<QT>(&sV[gs][Lay<D>::q(16 * w + c, g * QL)]);
@@ -385,12 +418,12 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
           const QT da = ld_shared<QT>(&tdo[Lay<D>::q(ql, g * QL)]);
           const f32x4 nl = *reinterpret_cast<const f32x4*>(&sL[buf][r0]);
           const f32x4 nd = *reinterpret_cast<const f32x4*>(&sDl[buf][r0]);
-          const f32x4 s = DOp<D>::mma(qa, kb, nl);         // q.k - lse/scale
+          const f32x4 sv = DOp<D>::mma(qa, kb, nl);        // q.k - lse/scale
           const f32x4 dp = DOp<D>::mma(da, vb, nd);        // dP - delta
           float p[4], ds[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float x = fmaf(s[i], c1, bb[qb][i]);
+            float x = fmaf(sv[i], c1, bb[qb][i]);
             if (MASK) x += mk2[gs];
             p[i] = __builtin_amdgcn_exp2f(x);
             ds[i] = p[i] * dp[i];
@@ -406,7 +439,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries of this half
         const u32x4 bp = u32x4{pP[0][0], pP[0][1], pP[1][0], pP[1][1]};
         const u32x4 bs = u32x4{pS[0][0], pS[0][1], pS[1][0], pS[1][1]};
-        *reinterpret_cast<u32x4*>(&sdS[buf][(16 * w + c) * SP + 32 * st + 8 * g]) = bs;
+        *reinterpret_cast<u32x4*>(&sdS[dsb][(16 * w + c) * SP + 32 * st + 8 * g]) = bs;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int qr = 32 * st + 8 * g + trk, qc = 16 * db + 4 * tra;
@@ -418,25 +451,32 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         }
       }
 
-      if (gs + 1 < G || j + 1 < nqt) {
-        stage(buf ^ 1);       // register-held parts of the next stage (all of it on the register path)
-        if (gs == G - 1) stage_bias((j + 1) & 1);
-      }
-      // the direct LDS loads of the next stage were issued by this wave after the
-      // previous barrier; they must land before any wave reads them
-      if (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-      __syncthreads();          // this stage's dS^T complete; next stage's tiles visible
-
-      // the stage two ahead: (j, gs + 2) or (j + 1, gs + 2 - G)
-      const int j2 = gs + 2 < G ? j : j + 1, g2 = gs + 2 < G ? gs + 2 : gs + 2 - G;
       if (VEC) {
-        // it goes into the buffer this stage released; the bias of tile j+1 (needed
-        // after the last stage of tile j) is fetched one stage ahead
-        if (j2 < nqt) load_stage(j2, g2, buf);
-        if (gs == G - 2 && j + 1 < nqt) load_bias(j + 1, (j + 1) & 1);
+        // the set that loaded stage s+1 waits for it and stages its -lse/-delta; the
+        // other set's loads (stage s+2) stay in flight across this barrier
+        const bool mine = lset == ((r + 1) & 1);
+        if (mine) {
+          __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+          if (s + 1 < nst) write_rls((r + 1) % 3);
+        }
+        lds_barrier();          // this stage's dS^T complete; stage s+1 visible
+        // the same set now loads stage s+3 into the buffer stage s released, and with
+        // it the bias of the query tile that starts there
+        if (mine && s + 3 < nst) {
+          const int j3 = j + (gs + 3) / G, g3 = (gs + 3) % G;
+          load_stage_direct(j3, g3, r % 3);
+          if (g3 == 0) load_bias_direct(j3, j3 & 1);
+        }
       } else {
-        if (j2 < nqt) load_stage(j2, g2, 0);
-        if (gs == G - 1 && j + 2 < nqt) load_bias(j + 2, 0);
+        if (s + 1 < nst) {
+          stage_regs(buf ^ 1);
+          if (gs == G - 1) stage_bias_regs((j + 1) & 1);
+        }
+        __syncthreads();        // this stage's dS^T complete; next stage's tiles visible
+        // the stage two ahead: (j, gs + 2) or (j + 1, gs + 2 - G)
+        const int j2 = gs + 2 < G ? j : j + 1, g2 = gs + 2 < G ? gs + 2 : gs + 2 - G;
+        if (j2 < nqt) load_stage_regs(j2, g2);
+        if (gs == G - 1 && j + 2 < nqt) load_bias_regs(j + 2);
       }
     }
 
@@ -451,9 +491,9 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int r = j * TQ + 32 * (qb >> 1) + 4 * (qb & 1) + i;   // row of group g = 0
+            const int rr = j * TQ + 32 * (qb >> 1) + 4 * (qb & 1) + i;   // row of group g = 0
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dbacc[qb][i]), rs, lane_off,
-                                                  (int)((uint32_t)r * N * 4), 0);
+                                                  (int)((uint32_t)rr * N * 4), 0);
           }
       } else {
 #pragma unroll
@@ -467,11 +507,22 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       }
     }
   };
-  if (nsl == G) {
-    for (int j = 0; j < nqt; ++j) query_tile(j, std::true_type{});
-  } else {
-    for (int j = 0; j < nqt; ++j) query_tile(j, std::false_type{});
-  }
+  using R0a = std::integral_constant<int, 0>;
+  using R0b = std::integral_constant<int, G>;
+  using R0c = std::integral_constant<int, 2 * G>;
+  auto run = [&](auto full_c) {
+    if (VEC) {
+      for (int j0 = 0; j0 < nqt; j0 += 3) {
+        query_tile(j0, full_c, R0a{});
+        if (j0 + 1 < nqt) query_tile(j0 + 1, full_c, R0b{});
+        if (j0 + 2 < nqt) query_tile(j0 + 2, full_c, R0c{});
+      }
+    } else {
+      for (int j = 0; j < nqt; ++j) query_tile(j, full_c, R0a{});
+    }
+  };
+  if (nsl == G) run(std::true_type{});
+  else run(std::false_type{});
   dq_stage(nqt - 1, G - 1, (G - 1) & 1, true);
 
   // epilogue: dK = scale * dK^T^T, dV
