@@ -326,12 +326,17 @@ def main():
 
 
 def kernel_hash():
-    """Hash of the kernel sources: stored traffic counters are valid only for the same code."""
+    """Hash of the kernel sources without comments and whitespace: stored traffic counters
+    are valid only for the same code (a comment edit keeps them)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "triangular_attention_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        txt = open(os.path.join(csrc, f), encoding="utf-8").read()
+        txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+        txt = re.sub(r"//[^\n]*", " ", txt)
+        h.update(f.encode() + b"\0" + " ".join(txt.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -19,14 +19,16 @@
 // as the accumulator inputs of the S and dP products, so the exponent costs
 // one FMA per score.
 //
-// Pipeline: stages (query tile j, slice g) are double-buffered in LDS with one
-// barrier per stage; the dQ product of stage i runs in stage i+1, in the same
-// straight-line block as that stage's score work, so every barrier interval
-// mixes VALU-heavy and MFMA-heavy work.
+// Pipeline: one barrier per stage (query tile j, slice g); the dQ product of
+// stage i runs in stage i+1, in the same straight-line block as that stage's
+// score work, so every barrier interval mixes VALU-heavy and MFMA-heavy work.
+// With N % 8 == 0 the Q, dO and bias tiles go from memory straight into LDS:
+// three stage buffers, loaded by two alternating sets of waves, so that each
+// load has two stages to land and a wave waits on memory at every other
+// barrier only.  Otherwise the stages go through registers, double-buffered.
 // Global reads are raw buffer loads with per-slice extents: rows past N read
 // as zero, which makes their probabilities irrelevant (dO, Q and K are zero
-// there) without per-load bounds checks.  With N % 8 == 0 the Q, dO and bias
-// tiles go from memory straight into LDS.
+// there) without per-load bounds checks.
 //
 // LDS layouts (bank conflicts of each access shape were measured on gfx950
 // with probe kernels replaying the exact lane addresses).  D = 32: Q, dO and K
