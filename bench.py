@@ -23,7 +23,9 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published 8 TB/s)
-KERNELS = ("fwd", "delta", "bwd", "reduce_dq", "reduce_dbias")
+# the dbias reduction runs first: measured, the dQ reduction streams 10% faster after it
+# than straight after the backward, and the dbias reduction loses less in that place
+KERNELS = ("fwd", "delta", "bwd", "reduce_dbias", "reduce_dq")
 
 
 def parse():

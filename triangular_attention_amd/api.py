@@ -158,8 +158,10 @@ def backward(q, k, v, bias, mask, scale, o, o_res, lse, d_o, workspace_buffers=N
     tri_attn_bwd(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv, dq_part, db_part)
     dq = torch.empty_like(q)
     dbias = torch.empty_like(bias)
-    tri_attn_reduce_dq(d, dq_part, dq)
+    # independent reductions; this order measured faster (the dQ reduction streams
+    # better after the dbias reduction than straight after the backward)
     tri_attn_reduce_dbias(d, db_part, dbias)
+    tri_attn_reduce_dq(d, dq_part, dq)
     return dq, dk, dv, dbias
 
 
