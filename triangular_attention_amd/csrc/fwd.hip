@@ -14,10 +14,11 @@
 // Data movement: everything a key tile needs (K, V, the 64 mask values and
 // the block's 128 x 64 bias tile) is requested one tile ahead with direct
 // global->LDS loads into double-buffered LDS, so the loop has no register
-// prefetch and one wait (all loads done) plus one barrier per tile.  The
-// memory pipeline, not the ALUs, limits this kernel: per-lane 16-byte loads
-// of mask and bias from every wave cost more address-unit time than the
-// arithmetic, so the per-key mask is loaded once per workgroup.
+// prefetch and one wait (all loads done) plus one barrier per tile.  Per-lane
+// 16-byte loads of mask and bias from every wave cost more address-unit time
+// than the arithmetic they feed, so the per-key mask is loaded once per
+// workgroup.  The loads and their wait remain the largest single cost; the
+// exponentials and the matrix products follow.
 //
 // Score arithmetic, kept short:
 //  * bias and mask enter through one exact matrix product per score block:
@@ -324,7 +325,8 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
       // probabilities relative to mref, packed to bf16, and their column sums
       auto probs = [&]() {
         const float nm = -mref[qb] * kLog2e;
-        float ts = 0.f;
+        // four independent partial sums (by row i of the 4-row groups), combined in a fixed tree
+        float ts[4];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           float p[2][4];
@@ -333,12 +335,12 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               p[e][i] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][m][e][i], kLog2e, nm));
-              ts += p[e][i];
+              ts[i] = (m == 0 && e == 0) ? p[e][i] : ts[i] + p[e][i];
             }
           pp[m] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
                         pack_bf16(p[1][2], p[1][3])};
         }
-        return ts;
+        return (ts[0] + ts[1]) + (ts[2] + ts[3]);
       };
       // new reference maximum: the tile's maximum (or the old one if larger)
       auto rebase = [&]() {
