@@ -31,7 +31,8 @@ CASES = [
     (12, 200, 2, 32, 0.0, 1.0, 1),     # 4 key tiles, 4 query tiles, 2 query tiles of the forward
     (10, 130, 2, 16, 0.1, 2.0, 1),     # D = 16, masked, ragged
     (7, 64, 2, 32, 0.0, 1.0, 1),       # no mask, N % 8 == 0, last group of 3 slices
-    (6, 48, 2, 16, 0.0, 2.0, 1),       # D = 16, no mask, N % 8 == 0, last group of 2 slices
+    (6, 48, 2, 16, 0.0, 2.0, 1),       # D = 16, no mask, N % 8 == 0, one group of 6 slices
+    (8, 96, 2, 16, 0.15, 1.0, 1),      # D = 16, masked, N % 8 == 0, groups of 6 and 2 slices
 ]
 
 

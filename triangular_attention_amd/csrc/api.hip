@@ -27,7 +27,8 @@ tri_attn_status check_dims(const tri_attn_dims* d) {
 }
 
 int64_t n_key_tiles(const tri_attn_dims* d) { return (d->N + tri::kBwdKeyTile - 1) / tri::kBwdKeyTile; }
-int64_t n_groups(const tri_attn_dims* d) { return (d->N_o + tri::kBwdGroup - 1) / tri::kBwdGroup; }
+int64_t group_size(const tri_attn_dims* d) { return tri::bwd_group((int)d->D, d->N % 8 == 0); }
+int64_t n_groups(const tri_attn_dims* d) { return (d->N_o + group_size(d) - 1) / group_size(d); }
 int64_t x_elems(const tri_attn_dims* d) { return d->B * d->N_o * d->H * d->N * d->D; }
 int64_t y_elems(const tri_attn_dims* d) { return d->B * d->H * d->N * d->N; }
 
@@ -61,7 +62,7 @@ tri_attn_status tri_attn_workspace(const tri_attn_dims* d, int64_t* dq_partial_e
   if (j_k) *j_k = n_key_tiles(d);
   if (l) *l = n_groups(d);
   if (key_tile) *key_tile = tri::kBwdKeyTile;
-  if (outer_group) *outer_group = tri::kBwdGroup;
+  if (outer_group) *outer_group = group_size(d);
   return TRI_ATTN_OK;
 }
 

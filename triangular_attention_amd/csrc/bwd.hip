@@ -51,6 +51,7 @@ namespace tri {
 template <int D> struct Lay;
 template <> struct Lay<32> {
   static constexpr int kRowElems = 32;
+  static constexpr int kKVRowElems = 32;
   __device__ static __forceinline__ int swq(int row) { return ((row >> 3) & 1) << 1 | ((row >> 4) & 1); }
   __device__ static __forceinline__ int swk(int row) { return (row >> 2) & 3; }
   __device__ static __forceinline__ int q(int row, int col) {
@@ -59,14 +60,25 @@ template <> struct Lay<32> {
   __device__ static __forceinline__ int k(int row, int col) {
     return row * 32 + ((((col >> 3) ^ swk(row)) & 3) << 3) + (col & 7);
   }
+  __device__ static __forceinline__ int v(int row, int col) { return q(row, col); }
   // logical chunk stored in physical slot `pchunk` of `row`
   __device__ static __forceinline__ int q_src_chunk(int row, int pchunk) { return (pchunk ^ swq(row)) & 3; }
   static constexpr int kSlotsPerRow = 4;
 };
 template <> struct Lay<16> {
-  static constexpr int kRowElems = 24;
+  static constexpr int kRowElems = 24;       // Q / dO rows padded to 48 bytes
+  static constexpr int kKVRowElems = 16;     // K / V rows unpadded (32 bytes)
   __device__ static __forceinline__ int q(int row, int col) { return row * 24 + col; }
-  __device__ static __forceinline__ int k(int row, int col) { return row * 24 + col; }
+  // K and V: in every 16-row group rows 8..11 and 12..15 trade places (row bit 2
+  // flipped where bit 3 is set) and the four 8-byte units of those rows are
+  // permuted by an XOR with 2, so that both the row reads (16 rows x 2 units per
+  // half-wave) and the transposing reads (rows 0..3 and 8..11 of a 16-row group)
+  // touch 64 distinct banks
+  __device__ static __forceinline__ int k(int row, int col) {
+    const int hi = (row >> 3) & 1;
+    return (row ^ (hi << 2)) * 16 + ((((col >> 2) ^ (hi << 1)) & 3) << 2) + (col & 3);
+  }
+  __device__ static __forceinline__ int v(int row, int col) { return k(row, col); }
   __device__ static __forceinline__ int q_src_chunk(int row, int pchunk) { return pchunk < 2 ? pchunk : 0; }
   static constexpr int kSlotsPerRow = 3;     // two data chunks and one padding chunk
 };
@@ -75,11 +87,14 @@ template <int D, bool MASK, bool VEC, int TK>
 __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int NW = TK / 16;     // waves; wave w owns keys 16w..16w+15 of the tile
   constexpr int NT = NW * 64;
-  constexpr int TQ = kBwdQueryTile, G = kBwdGroup;
+  constexpr int TQ = kBwdQueryTile, G = bwd_group(D, VEC);
   static_assert(G >= 2 && G % 2 == 0, "stage parity must repeat with every query tile");
-  constexpr int NB = VEC ? 3 : 2;  // Q / dO / -lse / -delta stage buffers
+  // Q / dO / -lse / -delta stage buffers: two on the register path, three on the
+  // direct path (stage s uses buffer s % NB)
+  constexpr int NB = VEC ? 3 : 2;
   constexpr int HW = NW / 2;      // waves per loader set (direct path)
-  constexpr int RE = Lay<D>::kRowElems;   // LDS elements per Q / dO / K row
+  constexpr int RE = Lay<D>::kRowElems;   // LDS elements per Q / dO row
+  constexpr int KRE = Lay<D>::kKVRowElems;  // LDS elements per K / V row
   constexpr int SP = TQ + 8;      // dS^T tile pitch (row = key)
   constexpr int CH = D / 8;       // 16-byte chunks per row in memory
   constexpr int NDB = D / 16;
@@ -97,8 +112,8 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) float sL[NB][TQ];    // -lse / scale of the stage's rows
   __shared__ __align__(16) float sDl[NB][TQ];   // -delta
   __shared__ __align__(16) uint16_t sdS[2][TK * SP];
-  __shared__ __align__(16) uint16_t sK[G][TK * RE];
-  __shared__ __align__(16) uint16_t sV[G][TK * RE];   // V rows of the key tile (row-read layout)
+  __shared__ __align__(16) uint16_t sK[G][TK * KRE];
+  __shared__ __align__(16) uint16_t sV[G][TK * KRE];   // V rows of the key tile (row-read layout)
   __shared__ __align__(16) uint16_t sB[2][TQ * TK];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
@@ -162,7 +177,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       const u32x4 kv = buf_ld16(rk, off);
       const u32x4 vv = buf_ld16(rv, off);
       *reinterpret_cast<u32x4*>(&sK[gs][Lay<D>::k(r, ch * 8)]) = kv;
-      *reinterpret_cast<u32x4*>(&sV[gs][Lay<D>::q(r, ch * 8)]) = vv;
+      *reinterpret_cast<u32x4*>(&sV[gs][Lay<D>::v(r, ch * 8)]) = vv;
     }
   }
 
@@ -375,8 +390,8 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
 
   // one query tile: its G stages and its dbias tile.  FULL: all G slices of the group
   // exist (every group but a ragged last one), so every stage's dS enters the dbias tile.
-  // R0: position of the tile's first stage in the 3-tile cycle of direct-path buffers
-  // (stage s uses buffer s % 3; tiles come in triples, so R0 is 0, G or 2G).
+  // R0: position of the tile's first stage in the cycle of direct-path buffers (stage s
+  // uses buffer s % NB; with G % NB != 0 tiles come in triples, so R0 is 0, G or 2G).
   auto query_tile = [&](int j, auto full_c, auto r0_c) {
     constexpr bool FULL = decltype(full_c)::value;
     constexpr int R0 = decltype(r0_c)::value;
@@ -395,7 +410,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     for (int gs = 0; gs < G; ++gs) {
       const int r = R0 + gs;                 // stage index modulo 3 * G
       const int s = G * j + gs;              // stage index
-      const int buf = VEC ? r % 3 : gs & 1;  // Q / dO / -lse / -delta buffer
+      const int buf = VEC ? r % NB : gs & 1;  // Q / dO / -lse / -delta buffer
       const int dsb = gs & 1;                // dS^T buffer
       const uint16_t* tq = sQ[buf];
       const uint16_t* tdo = sdO[buf];
@@ -407,7 +422,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       else dq_stage(j > 0 ? j - 1 : 0, G - 1, dsb ^ 1, j > 0);
 
       const QT kb = ld_shared<QT>(&sK[gs][Lay<D>::k(16 * w + c, g * QL)]);
-      const QT vb = ld_shared<QT>(&sV[gs][Lay<D>::q(16 * w + c, g * QL)]);
+      const QT vb = ld_shared<QT>(&sV[gs][Lay<D>::v(16 * w + c, g * QL)]);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         u32x2 pP[2], pS[2];
@@ -459,14 +474,14 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         const bool mine = lset == ((r + 1) & 1);
         if (mine) {
           __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-          if (s + 1 < nst) write_rls((r + 1) % 3);
+          if (s + 1 < nst) write_rls((r + 1) % NB);
         }
         lds_barrier();          // this stage's dS^T complete; stage s+1 visible
-        // the same set now loads stage s+3 into the buffer stage s released, and with
-        // it the bias of the query tile that starts there
+        // the same set now loads stage s+3 into its buffer (last used by stage s+3-NB,
+        // released by now), and with it the bias of the query tile that starts there
         if (mine && s + 3 < nst) {
           const int j3 = j + (gs + 3) / G, g3 = (gs + 3) % G;
-          load_stage_direct(j3, g3, r % 3);
+          load_stage_direct(j3, g3, (r + 3) % NB);
           if (g3 == 0) load_bias_direct(j3, j3 & 1);
         }
       } else {
@@ -513,7 +528,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   using R0b = std::integral_constant<int, G>;
   using R0c = std::integral_constant<int, 2 * G>;
   auto run = [&](auto full_c) {
-    if (VEC) {
+    if constexpr (VEC && G % NB != 0) {
       for (int j0 = 0; j0 < nqt; j0 += 3) {
         query_tile(j0, full_c, R0a{});
         if (j0 + 1 < nqt) query_tile(j0 + 1, full_c, R0b{});

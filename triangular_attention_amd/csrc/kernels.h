@@ -6,9 +6,12 @@
 namespace tri {
 
 // Tile constants of the key-tile backward.  J_K = ceil(N / kBwdKeyTile) dQ
-// partials and L = ceil(N_o / kBwdGroup) dbias partials.
+// partials and L = ceil(N_o / G) dbias partials, G = bwd_group(D, N % 8 == 0)
+// outer slices per workgroup: dK and dV of G slices stay in registers, so G is
+// 4 for D = 32 and 6 for D = 16 (half the accumulator registers per slice; 8
+// spills; the register-staged path for N % 8 != 0 has no room and keeps 4).
 constexpr int kBwdKeyTile = 128;
-constexpr int kBwdGroup = 4;
+constexpr int bwd_group(int D, bool vec) { return (D == 16 && vec) ? 6 : 4; }
 constexpr int kBwdQueryTile = 64;
 constexpr int kFwdQueryTile = 128;
 constexpr int kFwdKeyTile = 64;
