@@ -25,9 +25,9 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags.  The forward does VALU work on every MFMA result, so its
-# MFMA results stay in VGPRs; the backward keeps its long-lived dK/dV
-# accumulators in AGPRs (only MFMAs touch them until the epilogue).
+# Per-source extra flags.  Both kernels do VALU work on most MFMA results, so MFMA
+# results are formed in VGPRs (the register file is unified on gfx950: AGPRs would
+# not add capacity, only copies).
 EXTRA = {
     "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
