@@ -88,6 +88,9 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int NW = TK / 16;     // waves; wave w owns keys 16w..16w+15 of the tile
   constexpr int NT = NW * 64;
   constexpr int TQ = kBwdQueryTile, G = bwd_group(D, VEC);
+  constexpr int NQB = TQ / 16;    // 16-query blocks of a stage
+  constexpr int NST = TQ / 32;    // 32-query halves of a stage (dV / dK contraction steps)
+  static_assert(TQ % 32 == 0, "query tile must be whole 32-query halves");
   static_assert(G >= 2 && G % 2 == 0, "stage parity must repeat with every query tile");
   // Q / dO / -lse / -delta stage buffers: two on the register path, three on the
   // direct path (stage s uses buffer s % NB)
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int NBCH = TQ * TK / 8;   // 16-byte chunks of one bias tile
   constexpr int NR = (2 * NQCH + NT - 1) / NT;
   constexpr int NRB = (NBCH + NT - 1) / NT;
-  constexpr int NBLK = 4 * NDB;   // dQ output blocks per stage
+  constexpr int NBLK = NQB * NDB; // dQ output blocks per stage
   static_assert(NBLK <= NW, "one dQ block per wave at most");
   typedef typename DOp<D>::T QT;
   constexpr int QL = DOp<D>::kPerLane;
@@ -286,13 +289,14 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int BCH = TK / 8;                    // 16-byte slots per bias row
   constexpr int NBPIECE = TQ * BCH / 64;
   static_assert(TQ * BCH % 64 == 0, "bias tile must be whole wave pieces");
-  static_assert(!VEC || NBPIECE == 4 * HW, "four bias pieces per wave of loader set 0");
+  static_assert(NBPIECE % HW == 0, "bias pieces spread evenly over loader set 0");
+  constexpr int BPW = NBPIECE / HW;              // bias pieces per wave of set 0
   // direct path: the bias of a tile is loaded by set 0 (a tile starts at an even
   // stage); its wave ws loads pieces ws + k * NW/2.  Chunks of keys past N get an
   // offset past every extent and land as zeros (N % 8 == 0: a chunk is entirely in or out)
-  uint32_t boff[4];
+  uint32_t boff[BPW];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < BPW; ++k) {
     const int slot = (ws + k * HW) * 64 + lane, row = slot / BCH, ch = (slot % BCH) ^ (bsw(row) >> 1);
     const int k0 = t * TK + ch * 8;
     boff[k] = k0 < N ? (uint32_t)(row * N + k0) * 2 : 0xfffffff0u;
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     // descriptor from row j*TQ to row N of the (b, h) bias plane
     const u32x4 rw = make_rsrc_words(bias_plane + (int64_t)j * TQ * N, (uint32_t)(N - j * TQ) * N * 2);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) dma16(rw, sB[bbuf] + (ws + k * HW) * 512, boff[k]);
+    for (int k = 0; k < BPW; ++k) dma16(rw, sB[bbuf] + (ws + k * HW) * 512, boff[k]);
   };
   u32x4 rbt[VEC ? 1 : NRB];
   auto load_bias_regs = [&](int j) {
@@ -397,14 +401,14 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     constexpr int R0 = decltype(r0_c)::value;
     // bias * log2(e) of the lane's (query, key) pairs: one transposing read per block
     // gives rows 32s + 8g + 4e + 0..3 of block qb = 2s + e at the lane's key column
-    f32x4 bb[4];
+    f32x4 bb[NQB];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       const int r0 = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);
       const u32x2 bw = ds_read_tr(&sB[j & 1][b_at(r0 + trk, 16 * w + 4 * tra)]);
       bb[qb] = f32x4{bf_lo(bw[0]), bf_hi(bw[0]), bf_lo(bw[1]), bf_hi(bw[1])} * kLog2e;
     }
-    f32x4 dbacc[4];         // sum over the group's slices of the FP32 dS, in slice order
+    f32x4 dbacc[NQB];       // sum over the group's slices of the FP32 dS, in slice order
 
 #pragma unroll
     for (int gs = 0; gs < G; ++gs) {
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       const QT kb = ld_shared<QT>(&sK[gs][Lay<D>::k(16 * w + c, g * QL)]);
       const QT vb = ld_shared<QT>(&sV[gs][Lay<D>::v(16 * w + c, g * QL)]);
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < NST; ++st) {
         u32x2 pP[2], pS[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       if ((j + 1) * TQ <= N) {
         const uint32_t lane_off = (uint32_t)(8 * g * N + key) * 4;
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
+        for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int rr = j * TQ + 32 * (qb >> 1) + 4 * (qb & 1) + i;   // row of group g = 0
@@ -514,7 +518,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
           }
       } else {
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
+        for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int q = j * TQ + 32 * (qb >> 1) + 8 * g + 4 * (qb & 1) + i;
