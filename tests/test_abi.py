@@ -125,9 +125,10 @@ def test_workspace_matches_memory_table():
 
 def test_workspace_ragged():
     """Partial counts for ragged shapes.  The outer group is 4 slices except on the direct-load
-    path with D = 16 (N % 8 == 0), where the smaller accumulators leave room for 6."""
+    path with D = 16 (N even), where the smaller accumulators leave room for 6."""
     from triangular_attention_amd import api
-    for (N_o, N, D, G) in ((10, 65, 16, 4), (10, 64, 16, 6), (10, 64, 32, 4), (13, 200, 16, 6), (13, 201, 32, 4)):
+    for (N_o, N, D, G) in ((10, 65, 16, 4), (10, 64, 16, 6), (10, 66, 16, 6), (10, 64, 32, 4), (13, 200, 16, 6),
+                           (13, 201, 32, 4)):
         ws = api.workspace(_dims(B=2, N_o=N_o, H=3, N=N, D=D))
         jk, L = -(-N // ws["key_tile"]), -(-N_o // G)
         assert ws["outer_group"] == G and ws["key_tile"] == 128

@@ -21,18 +21,21 @@ TOL_O = 5e-3
 TOL_G = 1.5e-2
 
 # (N_o, N, H, D, mask_p, bias_std, B): several tiles, ragged tails, both D, masks,
-# N not a multiple of 8 (scalar-load path), an incomplete last outer group
+# all three bias-load paths (16-byte direct loads for N % 8 == 0, 4-byte direct loads
+# for other even N, registers for odd N) and incomplete last outer groups
 CASES = [
     (32, 32, 2, 16, 0.0, 1.0, 1),      # the tiny workload's shape, bf16-rounded
-    (8, 1, 2, 32, 0.0, 1.0, 1),        # a single key
-    (6, 33, 2, 16, 0.2, 1.0, 1),       # ragged, N % 8 != 0, last group of 2 slices
+    (8, 1, 2, 32, 0.0, 1.0, 1),        # a single key (odd N)
+    (6, 33, 2, 16, 0.2, 1.0, 1),       # odd N (register path), last group of 2 slices
     (9, 72, 3, 32, 0.1, 1.0, 1),       # ragged tail inside a 64-key tile, N % 8 == 0
-    (5, 100, 2, 32, 0.3, 2.0, 2),      # N % 8 != 0, B = 2, masked
+    (5, 100, 2, 32, 0.3, 2.0, 2),      # N % 8 == 4 (4-byte loads), B = 2, masked
     (12, 200, 2, 32, 0.0, 1.0, 1),     # 4 key tiles, 4 query tiles, 2 query tiles of the forward
-    (10, 130, 2, 16, 0.1, 2.0, 1),     # D = 16, masked, ragged
+    (10, 130, 2, 16, 0.1, 2.0, 1),     # D = 16, masked, N % 8 == 2 (4-byte loads)
     (7, 64, 2, 32, 0.0, 1.0, 1),       # no mask, N % 8 == 0, last group of 3 slices
     (6, 48, 2, 16, 0.0, 2.0, 1),       # D = 16, no mask, N % 8 == 0, one group of 6 slices
     (8, 96, 2, 16, 0.15, 1.0, 1),      # D = 16, masked, N % 8 == 0, groups of 6 and 2 slices
+    (7, 134, 3, 32, 0.0, 1.0, 1),      # no mask, N % 8 == 6 (4-byte loads), two key tiles
+    (9, 67, 2, 32, 0.2, 1.0, 1),       # odd N, masked, D = 32
 ]
 
 

@@ -27,7 +27,7 @@ tri_attn_status check_dims(const tri_attn_dims* d) {
 }
 
 int64_t n_key_tiles(const tri_attn_dims* d) { return (d->N + tri::kBwdKeyTile - 1) / tri::kBwdKeyTile; }
-int64_t group_size(const tri_attn_dims* d) { return tri::bwd_group((int)d->D, d->N % 8 == 0); }
+int64_t group_size(const tri_attn_dims* d) { return tri::bwd_group((int)d->D, tri::bias_load_width((int)d->N) != 0); }
 int64_t n_groups(const tri_attn_dims* d) { return (d->N_o + group_size(d) - 1) / group_size(d); }
 int64_t x_elems(const tri_attn_dims* d) { return d->B * d->N_o * d->H * d->N * d->D; }
 int64_t y_elems(const tri_attn_dims* d) { return d->B * d->H * d->N * d->N; }

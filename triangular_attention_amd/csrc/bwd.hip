@@ -22,10 +22,10 @@
 // Pipeline: one barrier per stage (query tile j, slice g); the dQ product of
 // stage i runs in stage i+1, in the same straight-line block as that stage's
 // score work, so every barrier interval mixes VALU-heavy and MFMA-heavy work.
-// With N % 8 == 0 the Q, dO and bias tiles go from memory straight into LDS:
+// With N even the Q, dO and bias tiles go from memory straight into LDS:
 // three stage buffers, loaded by two alternating sets of waves, so that each
 // load has two stages to land and a wave waits on memory at every other
-// barrier only.  Otherwise the stages go through registers, double-buffered.
+// barrier only.  With N odd the stages go through registers, double-buffered.
 // Global reads are raw buffer loads with per-slice extents: rows past N read
 // as zero, which makes their probabilities irrelevant (dO, Q and K are zero
 // there) without per-load bounds checks.
@@ -83,8 +83,11 @@ template <> struct Lay<16> {
   static constexpr int kSlotsPerRow = 3;     // two data chunks and one padding chunk
 };
 
-template <int D, bool MASK, bool VEC, int TK>
+// LD: how the bias tile reaches LDS.  16: 16-byte direct loads (N % 8 == 0); 4: 4-byte
+// direct loads, one per 256-byte bias row (N even); 0: through registers (N odd).
+template <int D, bool MASK, int LD, int TK>
 __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
+  constexpr bool VEC = LD != 0;   // direct global->LDS path
   constexpr int NW = TK / 16;     // waves; wave w owns keys 16w..16w+15 of the tile
   constexpr int NT = NW * 64;
   constexpr int TQ = kBwdQueryTile, G = bwd_group(D, VEC);
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   // The buffer descriptors start at the tile's first row and end at row N, so the
   // per-lane offsets do not depend on the stage and rows past N read as zero.
   //
-  // Direct path (N % 8 == 0): stage s goes from memory straight into LDS buffer s % 3.
+  // Direct path (N even): stage s goes from memory straight into LDS buffer s % 3.
   // The waves form two loader sets (waves 0..NW/2-1 and NW/2..NW-1); set s % 2 loads
   // stage s right after the barrier that ends stage s - 3 and waits for it (vmcnt(0))
   // only at the end of stage s - 1, so every load has two stages of compute to land,
@@ -220,7 +223,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       // would need a loop over its distinct values)
       const __amdgpu_buffer_rsrc_t rsl = make_rsrc(a.lse + sr, lext);
       const __amdgpu_buffer_rsrc_t rsd = make_rsrc(a.delta + sr, lext);
-      if (VEC) {
+      if (LD == 16) {     // rows of lse / delta 16-byte aligned (N % 4 == 0)
         if (lane < TQ / 4) rls = __builtin_bit_cast(f32x4, buf_ld16(rsl, q0 * 4));
         else rls = __builtin_bit_cast(f32x4, buf_ld16(rsd, q0 * 4));
       } else {
@@ -291,21 +294,42 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   static_assert(TQ * BCH % 64 == 0, "bias tile must be whole wave pieces");
   static_assert(NBPIECE % HW == 0, "bias pieces spread evenly over loader set 0");
   constexpr int BPW = NBPIECE / HW;              // bias pieces per wave of set 0
+  static_assert(LD != 4 || HW == 4, "4-byte bias loads: row bits 0-1 select the wave of set 0");
   // direct path: the bias of a tile is loaded by set 0 (a tile starts at an even
-  // stage); its wave ws loads pieces ws + k * NW/2.  Chunks of keys past N get an
-  // offset past every extent and land as zeros (N % 8 == 0: a chunk is entirely in or out)
-  uint32_t boff[BPW];
+  // stage).  LD 16: wave ws loads 1 KB pieces ws + k * NW/2.  LD 4: wave ws loads rows
+  // ws + 4k, one 256-byte row per load; bsw of those rows takes two values (row bit 3),
+  // so two lane offsets serve them all.  Keys past N get an offset past every extent
+  // and land as zeros (a 16-byte chunk, or a 4-byte pair of keys, is entirely in or out).
+  constexpr int NBOFF = LD == 4 ? 2 : BPW;
+  uint32_t boff[NBOFF];
 #pragma unroll
-  for (int k = 0; k < BPW; ++k) {
-    const int slot = (ws + k * HW) * 64 + lane, row = slot / BCH, ch = (slot % BCH) ^ (bsw(row) >> 1);
-    const int k0 = t * TK + ch * 8;
-    boff[k] = k0 < N ? (uint32_t)(row * N + k0) * 2 : 0xfffffff0u;
+  for (int k = 0; k < NBOFF; ++k) {
+    if (LD == 4) {
+      const int unit = (lane >> 1) ^ ((ws << 2) | (k << 4));   // logical 8-byte unit of the lane's dword
+      const int k0 = t * TK + 4 * unit + 2 * (lane & 1);
+      boff[k] = k0 < N ? (uint32_t)k0 * 2 : 0xfffffff0u;
+    } else {
+      const int slot = (ws + k * HW) * 64 + lane, row = slot / BCH, ch = (slot % BCH) ^ (bsw(row) >> 1);
+      const int k0 = t * TK + ch * 8;
+      boff[k] = k0 < N ? (uint32_t)(row * N + k0) * 2 : 0xfffffff0u;
+    }
   }
   auto load_bias_direct = [&](int j, int bbuf) {
-    // descriptor from row j*TQ to row N of the (b, h) bias plane
-    const u32x4 rw = make_rsrc_words(bias_plane + (int64_t)j * TQ * N, (uint32_t)(N - j * TQ) * N * 2);
+    if (LD == 4) {
+      // one descriptor per row, from that row to row N (extent zero past N)
 #pragma unroll
-    for (int k = 0; k < BPW; ++k) dma16(rw, sB[bbuf] + (ws + k * HW) * 512, boff[k]);
+      for (int k = 0; k < TQ / HW; ++k) {
+        const int r = ws + k * HW, rows_left = N - j * TQ - r;
+        const u32x4 rw = make_rsrc_words(bias_plane + ((int64_t)j * TQ + r) * N,
+                                         rows_left > 0 ? (uint32_t)rows_left * N * 2 : 0u);
+        dma4(rw, sB[bbuf] + r * TK, boff[(k >> 1) & 1]);
+      }
+    } else {
+      // descriptor from row j*TQ to row N of the (b, h) bias plane
+      const u32x4 rw = make_rsrc_words(bias_plane + (int64_t)j * TQ * N, (uint32_t)(N - j * TQ) * N * 2);
+#pragma unroll
+      for (int k = 0; k < BPW; ++k) dma16(rw, sB[bbuf] + (ws + k * HW) * 512, boff[k]);
+    }
   };
   u32x4 rbt[VEC ? 1 : NRB];
   auto load_bias_regs = [&](int j) {
@@ -566,27 +590,32 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   }
 }
 
-template <int D, bool MASK, bool VEC>
+template <int D, bool MASK, int LD>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   constexpr int TK = kBwdKeyTile;
   const int64_t nunit = (int64_t)a.B * a.n_groups * a.H;
   const int64_t nblk = 8 * ((nunit + 7) / 8) * a.n_key_tiles;
-  hipLaunchKernelGGL((bwd_kernel<D, MASK, VEC, TK>), dim3((unsigned)nblk), dim3(TK * 4), 0, s, a);
+  hipLaunchKernelGGL((bwd_kernel<D, MASK, LD, TK>), dim3((unsigned)nblk), dim3(TK * 4), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t s) {
-  const bool mask = a.mask != nullptr, vec = (a.N % 8) == 0;
-#define TRI_BWD_CASE(DD, MM, VV) \
-  if (D == DD && mask == MM && vec == VV) return launch_bwd_t<DD, MM, VV>(a, s);
-  TRI_BWD_CASE(32, false, true)
-  TRI_BWD_CASE(32, true, true)
-  TRI_BWD_CASE(32, false, false)
-  TRI_BWD_CASE(32, true, false)
-  TRI_BWD_CASE(16, false, true)
-  TRI_BWD_CASE(16, true, true)
-  TRI_BWD_CASE(16, false, false)
-  TRI_BWD_CASE(16, true, false)
+  const bool mask = a.mask != nullptr;
+  const int ld = bias_load_width(a.N);
+#define TRI_BWD_CASE(DD, MM, LL) \
+  if (D == DD && mask == MM && ld == LL) return launch_bwd_t<DD, MM, LL>(a, s);
+  TRI_BWD_CASE(32, false, 16)
+  TRI_BWD_CASE(32, true, 16)
+  TRI_BWD_CASE(32, false, 4)
+  TRI_BWD_CASE(32, true, 4)
+  TRI_BWD_CASE(32, false, 0)
+  TRI_BWD_CASE(32, true, 0)
+  TRI_BWD_CASE(16, false, 16)
+  TRI_BWD_CASE(16, true, 16)
+  TRI_BWD_CASE(16, false, 4)
+  TRI_BWD_CASE(16, true, 4)
+  TRI_BWD_CASE(16, false, 0)
+  TRI_BWD_CASE(16, true, 0)
 #undef TRI_BWD_CASE
   return hipErrorInvalidValue;
 }

@@ -104,6 +104,13 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, const void* lds, uint32_t off)
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(m0), "v"(off), "s"(rsrc) : "memory");
 }
 
+// The 4-byte form (lane l's 4 bytes land at `lds + 4 * l`), for rows that are only
+// 4-byte aligned in memory.
+__device__ __forceinline__ void dma4(u32x4 rsrc, const void* lds, uint32_t off) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(lds);
+  asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"{m0}"(m0), "v"(off), "s"(rsrc) : "memory");
+}
+
 template <typename T> __device__ __forceinline__ T ld_shared(const uint16_t* p) {
   return *reinterpret_cast<const T*>(p);
 }

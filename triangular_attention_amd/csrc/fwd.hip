@@ -44,7 +44,9 @@
 
 namespace tri {
 
-template <int D, bool MASK, bool VEC>
+// LD: width of the direct global->LDS loads of bias rows and mask values.  16: 16-byte
+// loads (N % 8 == 0); 4: 4-byte loads (N even); 0: bias and mask through registers (N odd).
+template <int D, bool MASK, int LD>
 __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
   constexpr int TQ = kFwdQueryTile, TK = kFwdKeyTile;
   constexpr int KP = D;        // K / V tile pitch (bf16), one row per key, 16-byte chunks swizzled
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
   // only adds its key offset.  Everything a tile reads from LDS was requested one tile
   // earlier, and the only wait is vmcnt(0) before the barrier that ends each tile.
   constexpr uint32_t kOOB = 0xFFFFF000u;       // any offset past every buffer
-  constexpr bool LDSIN = VEC;                  // mask and bias through LDS (16-byte aligned rows)
+  constexpr bool LDSIN = LD != 0;              // mask and bias through LDS (aligned rows)
   constexpr bool MLDS = MASK && LDSIN;
   auto sw = [](int r) { return (r >> 3) & (CH - 1); };
   auto swb = [](int r) { return (r >> 1) & 7; };   // bias rows: 8 chunks of 8 keys
@@ -147,12 +149,23 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
     const int piece = NKPIECE == 4 ? w : (w & 1);
     const int row = piece * (64 / CH) + lane / CH, pos = lane % CH;
     kv_off = (uint32_t)(row * D + (pos ^ sw(row)) * 8) * 2;
-    m_off = (MLDS && lane < TK / 4) ? (uint32_t)lane * 16 : kOOB;
+    if (LD == 4) {
+      // 4-byte loads: one load fills two 128-byte bias rows 2i, 2i+1 of the wave; lane l
+      // takes row 2i + (l >> 5) and dword l & 31 of it, whose chunk position XOR swb =
+      // (l & 31) / 4 XOR (i & 7) names the keys: b_off[0] = the lane's row base, b_off[1]
+      // = its dword's byte offset before the XOR
+      m_off = MLDS ? (uint32_t)lane * 4 : kOOB;
+      b_off[0] = (uint32_t)(qt * TQ + 32 * w + (lane >> 5)) * N * 2;
+      b_off[1] = (uint32_t)(lane & 31) * 4;
+      b_off[2] = b_off[3] = 0;
+    } else {
+      m_off = (MLDS && lane < TK / 4) ? (uint32_t)lane * 16 : kOOB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rl = 8 * j + lane / 8, pos8 = lane % 8;   // row within the wave's 32
-      const int q = qt * TQ + 32 * w + rl;
-      b_off[j] = (uint32_t)q * N * 2 + (uint32_t)((pos8 ^ swb(rl)) * 16);
+      for (int j = 0; j < 4; ++j) {
+        const int rl = 8 * j + lane / 8, pos8 = lane % 8;   // row within the wave's 32
+        const int q = qt * TQ + 32 * w + rl;
+        b_off[j] = (uint32_t)q * N * 2 + (uint32_t)((pos8 ^ swb(rl)) * 16);
+      }
     }
   }
   // descriptor words for the untracked direct loads (used when every input of the
@@ -178,9 +191,29 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
     // the tile's 64 mask values: one wave, and only when there is a mask (these
     // loads are untracked, so the per-wave load count may differ)
     if constexpr (MLDS) {
-      if (w == 0) dma16(wM, dM, real && m_off != kOOB ? (uint32_t)(kt * TK) * 4 + m_off : kOOB);
+      if (LD == 4) {
+        // 64 mask values, one per lane; keys past N read past the extent as zeros
+        if (w == 0) dma4(wM, dM, real ? (uint32_t)(kt * TK) * 4 + m_off : kOOB);
+      } else {
+        if (w == 0) dma16(wM, dM, real && m_off != kOOB ? (uint32_t)(kt * TK) * 4 + m_off : kOOB);
+      }
     }
-    if constexpr (LDSIN) {
+    if constexpr (LD == 4) {
+      // keys past N (last tile only) must read as zero: pairs of keys are entirely in or
+      // out (N even), and rows past N fall outside the plane's extent
+      const int klim = N - kt * TK;       // keys of this tile inside N
+      // the 16 offsets are formed here from opaque copies of the lane bases, so that the
+      // compiler does not hoist them out of the loop into 16 more live registers
+      uint32_t rowb = b_off[0], dwb = b_off[1];
+      asm volatile("" : "+v"(rowb), "+v"(dwb));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t x = dwb ^ (uint32_t)(16 * (i & 7));     // byte offset of the lane's keys
+        const uint32_t off = rowb + (uint32_t)(2 * i) * N * 2 + (uint32_t)(kt * TK) * 2 + x;
+        const bool ok = real && (klim >= TK || (int)(x >> 1) < klim);
+        dma4(wB, dB + (32 * w + 2 * i) * TK, ok ? off : kOOB);
+      }
+    } else if constexpr (LDSIN) {
       const uint32_t bo = (uint32_t)(kt * TK) * 2;
 #pragma unroll
       for (int j = 0; j < 4; ++j) dma16(wB, dB + (32 * w + 8 * j) * TK, real ? bo + b_off[j] : kOOB);
@@ -195,27 +228,19 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
       const int kk = kt * TK + 32 * m + 8 * g;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        if (VEC) {
-          rb[qb][m] = buf_ld16(rB, boff[qb] + (uint32_t)kk * 2);
-        } else {
-          uint32_t wv[4];
+        uint32_t wv[4];   // odd N: rows are only 2-byte aligned
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const uint32_t o2 = boff[qb] + (uint32_t)(kk + 2 * p) * 2;
-            wv[p] = (uint32_t)buf_ld2(rB, o2) | ((uint32_t)buf_ld2(rB, o2 + 2) << 16);
-          }
-          rb[qb][m] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t o2 = boff[qb] + (uint32_t)(kk + 2 * p) * 2;
+          wv[p] = (uint32_t)buf_ld2(rB, o2) | ((uint32_t)buf_ld2(rB, o2 + 2) << 16);
         }
+        rb[qb][m] = u32x4{wv[0], wv[1], wv[2], wv[3]};
       }
       if (MASK) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          if (VEC) {
-            rm[m][e] = __builtin_bit_cast(f32x4, buf_ld16(rM, (uint32_t)(kk + 4 * e) * 4));
-          } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rm[m][e][i] = __uint_as_float(buf_ld4(rM, (uint32_t)(kk + 4 * e + i) * 4));
-          }
+          for (int i = 0; i < 4; ++i) rm[m][e][i] = __uint_as_float(buf_ld4(rM, (uint32_t)(kk + 4 * e + i) * 4));
         }
       }
     }
@@ -429,27 +454,32 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool MASK, bool VEC>
+template <int D, bool MASK, int LD>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   const int64_t nunit = (int64_t)a.B * a.N_o * a.H;
   const int64_t nqt = (a.N + kFwdQueryTile - 1) / kFwdQueryTile;
   const int64_t nblk = 8 * ((nunit + 7) / 8) * nqt;
-  hipLaunchKernelGGL((fwd_kernel<D, MASK, VEC>), dim3((unsigned)nblk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((fwd_kernel<D, MASK, LD>), dim3((unsigned)nblk), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int D, hipStream_t s) {
-  const bool mask = a.mask != nullptr, vec = (a.N % 8) == 0;
-#define TRI_FWD_CASE(DD, MM, VV) \
-  if (D == DD && mask == MM && vec == VV) return launch_fwd_t<DD, MM, VV>(a, s);
-  TRI_FWD_CASE(32, false, true)
-  TRI_FWD_CASE(32, true, true)
-  TRI_FWD_CASE(32, false, false)
-  TRI_FWD_CASE(32, true, false)
-  TRI_FWD_CASE(16, false, true)
-  TRI_FWD_CASE(16, true, true)
-  TRI_FWD_CASE(16, false, false)
-  TRI_FWD_CASE(16, true, false)
+  const bool mask = a.mask != nullptr;
+  const int ld = bias_load_width(a.N);
+#define TRI_FWD_CASE(DD, MM, LL) \
+  if (D == DD && mask == MM && ld == LL) return launch_fwd_t<DD, MM, LL>(a, s);
+  TRI_FWD_CASE(32, false, 16)
+  TRI_FWD_CASE(32, true, 16)
+  TRI_FWD_CASE(32, false, 4)
+  TRI_FWD_CASE(32, true, 4)
+  TRI_FWD_CASE(32, false, 0)
+  TRI_FWD_CASE(32, true, 0)
+  TRI_FWD_CASE(16, false, 16)
+  TRI_FWD_CASE(16, true, 16)
+  TRI_FWD_CASE(16, false, 4)
+  TRI_FWD_CASE(16, true, 4)
+  TRI_FWD_CASE(16, false, 0)
+  TRI_FWD_CASE(16, true, 0)
 #undef TRI_FWD_CASE
   return hipErrorInvalidValue;
 }

@@ -9,9 +9,13 @@ namespace tri {
 // partials and L = ceil(N_o / G) dbias partials, G = bwd_group(D, N % 8 == 0)
 // outer slices per workgroup: dK and dV of G slices stay in registers, so G is
 // 4 for D = 32 and 6 for D = 16 (half the accumulator registers per slice; 8
-// spills; the register-staged path for N % 8 != 0 has no room and keeps 4).
+// spills; the register-staged path for odd N has no room and keeps 4).
 constexpr int kBwdKeyTile = 128;
 constexpr int bwd_group(int D, bool vec) { return (D == 16 && vec) ? 6 : 4; }
+// Width of the direct global->LDS loads of bias rows (N bf16 per row): 16 bytes when
+// rows are 16-byte aligned, 4 bytes when they are 4-byte aligned, 0 = no direct loads
+// (odd N: rows go through registers).  `vec` above means a nonzero width.
+constexpr int bias_load_width(int N) { return N % 8 == 0 ? 16 : (N % 2 == 0 ? 4 : 0); }
 constexpr int kBwdQueryTile = 64;
 constexpr int kFwdQueryTile = 128;
 constexpr int kFwdKeyTile = 64;
