@@ -36,6 +36,8 @@ CASES = [
     (8, 96, 2, 16, 0.15, 1.0, 1),      # D = 16, masked, N % 8 == 0, groups of 6 and 2 slices
     (7, 134, 3, 32, 0.0, 1.0, 1),      # no mask, N % 8 == 6 (4-byte loads), two key tiles
     (9, 67, 2, 32, 0.2, 1.0, 1),       # odd N, masked, D = 32
+    (3, 63, 1, 16, 0.1, 1.0, 3),       # odd N, D = 16, one head, B = 3
+    (5, 50, 2, 16, 0.0, 1.0, 1),       # D = 16, no mask, N % 8 == 2 (4-byte loads)
 ]
 
 
