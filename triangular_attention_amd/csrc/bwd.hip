@@ -333,20 +333,30 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   };
   u32x4 rbt[VEC ? 1 : NRB];
   auto load_bias_regs = [&](int j) {
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias_plane + (int64_t)j * TQ * N, (uint32_t)(N - j * TQ) * N * 2);
+    // odd N: rows are only 2-byte aligned; the descriptor starts at the 4-byte boundary
+    // at or below the tile's first row (extra bytes earlier), 8 keys are read as five
+    // aligned dwords shifted into place, and keys past N are zeroed
+    const uint16_t* rowp = bias_plane + (int64_t)j * TQ * N;
+    const uint32_t extra = (uint32_t)((uintptr_t)rowp & 3u);
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc((const char*)rowp - extra, ((uint32_t)(N - j * TQ) * N * 2 + extra + 3u) & ~3u);
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
       const int ci = tid + r * NT;
       if (ci < NBCH) {
         const int row = ci / (TK / 8), ch = ci % (TK / 8);
         const int k0 = t * TK + ch * 8;
+        const uint32_t e0 = extra + (uint32_t)(row * N + k0) * 2;
+        const uint32_t a0 = e0 & ~3u, sh = (e0 & 2u) << 3;
+        uint32_t x[5];
+#pragma unroll
+        for (int p = 0; p < 5; ++p) x[p] = buf_ld4(rb, a0 + 4u * p);
         uint32_t wv[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int k_lo = k0 + 2 * p;
-          const uint32_t lo = k_lo < N ? buf_ld2(rb, (uint32_t)(row * N + k_lo) * 2) : 0u;
-          const uint32_t hi = k_lo + 1 < N ? buf_ld2(rb, (uint32_t)(row * N + k_lo + 1) * 2) : 0u;
-          wv[p] = lo | (hi << 16);
+          const uint32_t wd = __builtin_amdgcn_alignbit(x[p + 1], x[p], sh);
+          wv[p] = k_lo + 1 < N ? wd : (k_lo < N ? (wd & 0xffffu) : 0u);
         }
         rbt[r] = u32x4{wv[0], wv[1], wv[2], wv[3]};
       }

@@ -87,7 +87,13 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.q + slice * D, sbytes);
   const __amdgpu_buffer_rsrc_t rK = make_rsrc(a.k + slice * D, sbytes);
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(a.v + slice * D, sbytes);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.bias + ((int64_t)b * a.H + h) * N * N, (uint32_t)N * N * 2);
+  // register path (odd N): bias planes are only 2-byte aligned, so the descriptor starts
+  // at the 4-byte boundary at or below the plane (bextra bytes earlier) and the rows are
+  // read as aligned dwords and shifted into place
+  const uint16_t* bplane = a.bias + ((int64_t)b * a.H + h) * N * N;
+  const uint32_t bextra = (uint32_t)((uintptr_t)bplane & 3u);
+  const __amdgpu_buffer_rsrc_t rB =
+      make_rsrc((const char*)bplane - bextra, ((uint32_t)N * N * 2 + bextra + 3u) & ~3u);
   const __amdgpu_buffer_rsrc_t rM =
       make_rsrc(MASK ? (const void*)(a.mask + (int64_t)bo * N) : (const void*)a.q, MASK ? (uint32_t)N * 4 : 0u);
 
@@ -228,13 +234,14 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
       const int kk = kt * TK + 32 * m + 8 * g;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        uint32_t wv[4];   // odd N: rows are only 2-byte aligned
+        // 8 keys from a 2-byte aligned address: five aligned dwords, shifted by 0 or 16 bits
+        const uint32_t e0 = bextra + boff[qb] + (uint32_t)kk * 2;
+        const uint32_t a0 = e0 & ~3u, sh = (e0 & 2u) << 3;
+        uint32_t x[5];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t o2 = boff[qb] + (uint32_t)(kk + 2 * p) * 2;
-          wv[p] = (uint32_t)buf_ld2(rB, o2) | ((uint32_t)buf_ld2(rB, o2 + 2) << 16);
-        }
-        rb[qb][m] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        for (int p = 0; p < 5; ++p) x[p] = buf_ld4(rB, a0 + 4u * p);
+        rb[qb][m] = u32x4{__builtin_amdgcn_alignbit(x[1], x[0], sh), __builtin_amdgcn_alignbit(x[2], x[1], sh),
+                          __builtin_amdgcn_alignbit(x[3], x[2], sh), __builtin_amdgcn_alignbit(x[4], x[3], sh)};
       }
       if (MASK) {
 #pragma unroll
