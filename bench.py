@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--workload", default="n768_d32_mask")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-compensate", action="store_true", help="run without the output residual")
+    ap.add_argument("--partials", choices=("fp32", "bf16"), default="fp32",
+                    help="partial precision: fp32 (the reference contract) or the bf16-partial variant")
     ap.add_argument("--cpu-seconds", type=float, default=25.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -52,8 +54,9 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic(w, jk, L):
-    """Algorithmic flops and minimum HBM bytes of one launch of each kernel."""
+def algorithmic(w, jk, L, pb=4):
+    """Algorithmic flops and minimum HBM bytes of one launch of each kernel (pb = bytes per
+    partial element)."""
     X = w.B * w.N_o * w.H * w.N * w.D
     Y = w.B * w.H * w.N * w.N
     R = w.B * w.N_o * w.H * w.N
@@ -63,9 +66,9 @@ def algorithmic(w, jk, L):
         "fwd": {"flops": 4.0 * S * w.D, "bytes": 2 * (3 * X + Y + 2 * X) + 4 * (M + R)},
         "delta": {"flops": 2.0 * X, "bytes": 2 * 3 * X + 4 * R},
         "bwd": {"flops": 10.0 * S * w.D,
-                "bytes": 2 * (4 * X + Y + 2 * X) + 4 * (2 * R + M) + 4 * (jk * X + L * Y)},
-        "reduce_dq": {"flops": float(jk * X), "bytes": 4 * jk * X + 2 * X},
-        "reduce_dbias": {"flops": float(L * Y), "bytes": 4 * L * Y + 2 * Y},
+                "bytes": 2 * (4 * X + Y + 2 * X) + 4 * (2 * R + M) + pb * (jk * X + L * Y)},
+        "reduce_dq": {"flops": float(jk * X), "bytes": pb * jk * X + 2 * X},
+        "reduce_dbias": {"flops": float(L * Y), "bytes": pb * L * Y + 2 * Y},
     }
 
 
@@ -210,16 +213,19 @@ def main():
     delta = torch.empty_like(lse)
     dk, dv, dq = torch.empty_like(k), torch.empty_like(v), torch.empty_like(q)
     dbias = torch.empty_like(bias)
-    dqp = torch.empty(ws["dq_partial_elems"], dtype=torch.float32, device=dev)
-    dbp = torch.empty(ws["dbias_partial_elems"], dtype=torch.float32, device=dev)
+    bp = args.partials == "bf16"
+    pdt = torch.bfloat16 if bp else torch.float32
+    dqp = torch.empty(ws["dq_partial_elems"], dtype=pdt, device=dev)
+    dbp = torch.empty(ws["dbias_partial_elems"], dtype=pdt, device=dev)
     stream = torch.cuda.current_stream()
 
     calls = {
         "fwd": lambda: ta.tri_attn_fwd(d, q, k, v, bias, mask, o, o_res, lse, stream),
         "delta": lambda: ta.tri_attn_bwd_delta(d, o, o_res, do, delta, stream),
-        "bwd": lambda: ta.tri_attn_bwd(d, q, k, v, bias, mask, do, lse, delta, dk, dv, dqp, dbp, stream),
-        "reduce_dq": lambda: ta.tri_attn_reduce_dq(d, dqp, dq, stream),
-        "reduce_dbias": lambda: ta.tri_attn_reduce_dbias(d, dbp, dbias, stream),
+        "bwd": lambda: ta.tri_attn_bwd(d, q, k, v, bias, mask, do, lse, delta, dk, dv, dqp, dbp, stream,
+                                       bf16_partials=bp),
+        "reduce_dq": lambda: ta.tri_attn_reduce_dq(d, dqp, dq, stream, bf16_partials=bp),
+        "reduce_dbias": lambda: ta.tri_attn_reduce_dbias(d, dbp, dbias, stream, bf16_partials=bp),
     }
 
     def step():
@@ -256,7 +262,7 @@ def main():
         for i, n in enumerate(KERNELS):
             per[n] += evs[s][i].elapsed_time(evs[s][i + 1]) / args.steps
 
-    alg = algorithmic(w, ws["j_k"], ws["l"])
+    alg = algorithmic(w, ws["j_k"], ws["l"], 2 if bp else 4)
     kernels = {}
     for n in KERNELS:
         ms = per[n]
@@ -309,7 +315,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N_o": w.N_o, "N": w.N, "H": w.H, "D": w.D,
                    "scale": w.scale, "bias_std": w.bias_std, "mask_p": w.mask_p,
-                   "compensate": comp, "flops_per_step": w.flops_fwd_bwd,
+                   "compensate": comp, "partials": args.partials, "flops_per_step": w.flops_fwd_bwd,
                    "key_tile": ws["key_tile"], "outer_group": ws["outer_group"],
                    "description": w.description},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

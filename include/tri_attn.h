@@ -123,6 +123,27 @@ tri_attn_status tri_attn_reduce_dbias(const tri_attn_dims* d, const float* dbias
                                       tri_bf16* dbias, tri_attn_stream stream);
 
 /*
+ * BF16-partial variant (the pages size the partials in BF16, Table 2): the same
+ * three calls with the dQ and dbias partials stored as bf16 — each partial element
+ * is the FP32 value rounded once to bf16 (round to nearest even) before it is
+ * stored; the reductions add the partials in FP32 in the same fixed order.  Half
+ * the partial bytes, at the cost of one bf16 rounding per partial.  Buffers hold
+ * the element counts of tri_attn_workspace, 2 bytes each, 16-byte aligned.  The
+ * FP32 calls above remain the reference path.  Errors as for those calls.
+ */
+tri_attn_status tri_attn_bwd_bf16p(const tri_attn_dims* d,
+                                   const tri_bf16* q, const tri_bf16* k, const tri_bf16* v,
+                                   const tri_bf16* bias, const float* mask /* may be NULL */,
+                                   const tri_bf16* d_o, const float* lse, const float* delta,
+                                   tri_bf16* dk, tri_bf16* dv,
+                                   tri_bf16* dq_partial, tri_bf16* dbias_partial,
+                                   tri_attn_stream stream);
+tri_attn_status tri_attn_reduce_dq_bf16p(const tri_attn_dims* d, const tri_bf16* dq_partial,
+                                         tri_bf16* dq, tri_attn_stream stream);
+tri_attn_status tri_attn_reduce_dbias_bf16p(const tri_attn_dims* d, const tri_bf16* dbias_partial,
+                                            tri_bf16* dbias, tri_attn_stream stream);
+
+/*
  * Partial-buffer sizes for these dimensions (elements, FP32), the number of
  * key tiles J_K and of outer groups L, and the key-tile / group sizes used.
  * Any output pointer may be NULL.  Host-only arithmetic; no device access.

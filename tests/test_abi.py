@@ -19,7 +19,7 @@ def lib():
 def _header_symbols():
     txt = open(os.path.join(ROOT, "include", "tri_attn.h")).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(tri_attn_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(tri_attn_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -79,6 +79,13 @@ def test_validation_errors_before_launch(lib):
     assert lib.tri_attn_reduce_dq(ctypes.byref(d), P, MIS, None) == 4
     assert lib.tri_attn_reduce_dbias(ctypes.byref(d), P, None, None) == 1
     assert lib.tri_attn_reduce_dbias(ctypes.byref(_dims(H=0)), P, P, None) == 2
+    # the bf16-partial variant validates like the FP32 calls
+    assert lib.tri_attn_bwd_bf16p(ctypes.byref(d), P, P, P, P, None, P, P, P, P, P, P, None, None) == 1
+    assert lib.tri_attn_bwd_bf16p(ctypes.byref(d), P, P, P, P, None, P, P, P, P, P, MIS, P, None) == 4
+    assert lib.tri_attn_bwd_bf16p(ctypes.byref(_dims(D=64)), P, P, P, P, None, P, P, P, P, P, P, P, None) == 3
+    assert lib.tri_attn_reduce_dq_bf16p(ctypes.byref(d), None, P, None) == 1
+    assert lib.tri_attn_reduce_dq_bf16p(ctypes.byref(d), MIS, P, None) == 4
+    assert lib.tri_attn_reduce_dbias_bf16p(ctypes.byref(_dims(N=0)), P, P, None) == 2
 
 
 def test_python_binding_raises(lib):

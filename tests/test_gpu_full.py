@@ -123,3 +123,26 @@ def test_residual_compensation_ablation(name):
     print(name, "with residual", e_on, "without", e_off, flush=True)
     for n in ("dq", "dk", "dbias"):
         assert e_on[n] < e_off[n], (n, e_on[n], e_off[n])
+
+
+@pytest.mark.parametrize("name", ["n640_d16", "n768_d32_mask"])
+def test_bf16_partials_full_size(name):
+    """The bf16-partial variant at full size: sampled errors against the oracle within the
+    tolerance, next to those of the FP32-partial path on the same input (the accuracy cost
+    of halving the partial bytes)."""
+    ta = require_gpu()
+    w = synth.get(name)
+    print(f"bf16-partial full-size parity {name}", flush=True)
+    x = synth.make_inputs(w, 0)
+    dev = to_dev(x)
+    o, o_res, lse = ta.forward(dev["q"], dev["k"], dev["v"], dev["bias"], dev["mask"], w.scale)
+    args = (dev["q"], dev["k"], dev["v"], dev["bias"], dev["mask"], w.scale, o, o_res, lse, dev["do"])
+    errs = {}
+    for bf in (False, True):
+        dq, dk, dv, dbias = ta.backward(*args, bf16_partials=bf)
+        torch.cuda.synchronize()
+        got = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "dbias": dbias}
+        errs[bf] = _samples(w, x, got)
+    print(name, "fp32 partials", errs[False], "bf16 partials", errs[True], flush=True)
+    for n in ("dq", "dk", "dv", "dbias"):
+        assert errs[True][n] <= TOL_G, (n, errs[True])

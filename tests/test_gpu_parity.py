@@ -189,3 +189,30 @@ def test_python_validation_on_device():
     q64 = torch.zeros(1, 2, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ta.TriAttnError):
         ta.forward(q64, q64, q64, bias)
+
+
+@pytest.mark.parametrize("case", [(9, 72, 3, 32, 0.1, 1.0, 1), (5, 100, 2, 32, 0.3, 2.0, 2), (8, 96, 2, 16, 0.15, 1.0, 1),
+                                  (9, 67, 2, 32, 0.2, 1.0, 1)], ids=_id)
+def test_bf16_partials_variant_matches_oracle(case):
+    """The bf16-partial variant (tri_attn_bwd_bf16p and its reductions): every gradient within
+    the tolerance of the oracle, dK and dV bitwise equal to the FP32-partial path (they never
+    pass through a partial), and repeated calls bitwise identical."""
+    ta = require_gpu()
+    N_o, N, H, D, mask_p, bstd, B = case
+    w, _ = workload(N_o, N, H, D, mask_p, bstd, B=B)
+    x = inputs(w, seed=N * 7 + D + 1, mask_p=mask_p)
+    print(f"bf16 partials {_id(case)}", flush=True)
+    dev = to_dev(x)
+    mask = dev["mask"]
+    o, o_res, lse = ta.forward(dev["q"], dev["k"], dev["v"], dev["bias"], mask, w.scale)
+    args = (dev["q"], dev["k"], dev["v"], dev["bias"], mask, w.scale, o, o_res, lse, dev["do"])
+    g32 = ta.backward(*args)
+    g16 = ta.backward(*args, bf16_partials=True)
+    g16b = ta.backward(*args, bf16_partials=True)
+    torch.cuda.synchronize()
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["bias"], x["mask"], w.scale, x["do"])
+    for i, n in enumerate(("dq", "dk", "dv", "dbias")):
+        assert torch.equal(g16[i], g16b[i]), n
+        e = oracle.rel_rmse(np64(g16[i]), ref[n])
+        assert e <= TOL_G, (n, e)
+    assert torch.equal(g16[1], g32[1]) and torch.equal(g16[2], g32[2])

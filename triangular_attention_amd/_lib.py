@@ -28,6 +28,9 @@ EXPORTS = (
     "tri_attn_bwd",
     "tri_attn_reduce_dq",
     "tri_attn_reduce_dbias",
+    "tri_attn_bwd_bf16p",
+    "tri_attn_reduce_dq_bf16p",
+    "tri_attn_reduce_dbias_bf16p",
     "tri_attn_workspace",
     "tri_attn_status_string",
     "tri_attn_version",
@@ -73,6 +76,9 @@ def load() -> ctypes.CDLL:
         "tri_attn_bwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "tri_attn_reduce_dq": [dp, vp, vp, vp],
         "tri_attn_reduce_dbias": [dp, vp, vp, vp],
+        "tri_attn_bwd_bf16p": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "tri_attn_reduce_dq_bf16p": [dp, vp, vp, vp],
+        "tri_attn_reduce_dbias_bf16p": [dp, vp, vp, vp],
         "tri_attn_workspace": [dp, i64p, i64p, i64p, i64p, i64p, i64p],
     }
     for name, args in sig.items():

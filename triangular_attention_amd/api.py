@@ -89,7 +89,19 @@ def tri_attn_bwd_delta(d, o, o_res, d_o, delta, stream=None):
                                                             _ptr(delta), _stream(stream)))
 
 
-def tri_attn_bwd(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv, dq_partial, dbias_partial, stream=None):
+def _partial_dtype(bf16_partials):
+    return torch.bfloat16 if bf16_partials else torch.float32
+
+
+def _need_partial(t, name, dtype, elems):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous() \
+            or t.numel() < elems:
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor with >= {elems} elements")
+
+
+def tri_attn_bwd(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv, dq_partial, dbias_partial, stream=None,
+                 bf16_partials=False):
+    """Main backward; ``bf16_partials`` selects ``tri_attn_bwd_bf16p`` (bf16 partial buffers)."""
     B, N_o, H, N, D = d.B, d.N_o, d.H, d.N, d.D
     x = (B, N_o, H, N, D)
     for n, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o), ("dk", dk), ("dv", dv)):
@@ -100,33 +112,32 @@ def tri_attn_bwd(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv, dq_partial, db
     _need(lse, "lse", torch.float32, (B, N_o, H, N))
     _need(delta, "delta", torch.float32, (B, N_o, H, N))
     ws = workspace(d)
-    if dq_partial.dtype != torch.float32 or dq_partial.numel() < ws["dq_partial_elems"] or not dq_partial.is_contiguous():
-        raise ValueError(f"dq_partial must be contiguous float32 with >= {ws['dq_partial_elems']} elements")
-    if dbias_partial.dtype != torch.float32 or dbias_partial.numel() < ws["dbias_partial_elems"] or not dbias_partial.is_contiguous():
-        raise ValueError(f"dbias_partial must be contiguous float32 with >= {ws['dbias_partial_elems']} elements")
+    pdt = _partial_dtype(bf16_partials)
+    _need_partial(dq_partial, "dq_partial", pdt, ws["dq_partial_elems"])
+    _need_partial(dbias_partial, "dbias_partial", pdt, ws["dbias_partial_elems"])
     lib = _lib.load()
-    _lib.check("tri_attn_bwd", lib.tri_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
-                                                _ptr(d_o), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
-                                                _ptr(dq_partial), _ptr(dbias_partial), _stream(stream)))
+    name = "tri_attn_bwd_bf16p" if bf16_partials else "tri_attn_bwd"
+    _lib.check(name, getattr(lib, name)(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
+                                        _ptr(d_o), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
+                                        _ptr(dq_partial), _ptr(dbias_partial), _stream(stream)))
 
 
-def tri_attn_reduce_dq(d, dq_partial, dq, stream=None):
+def tri_attn_reduce_dq(d, dq_partial, dq, stream=None, bf16_partials=False):
+    """dQ from its partials; ``bf16_partials`` selects ``tri_attn_reduce_dq_bf16p``."""
     _need(dq, "dq", torch.bfloat16, (d.B, d.N_o, d.H, d.N, d.D))
-    ws = workspace(d)
-    if dq_partial.dtype != torch.float32 or dq_partial.numel() < ws["dq_partial_elems"] or not dq_partial.is_contiguous():
-        raise ValueError("dq_partial has the wrong dtype or size")
+    _need_partial(dq_partial, "dq_partial", _partial_dtype(bf16_partials), workspace(d)["dq_partial_elems"])
     lib = _lib.load()
-    _lib.check("tri_attn_reduce_dq", lib.tri_attn_reduce_dq(ctypes.byref(d), _ptr(dq_partial), _ptr(dq), _stream(stream)))
+    name = "tri_attn_reduce_dq_bf16p" if bf16_partials else "tri_attn_reduce_dq"
+    _lib.check(name, getattr(lib, name)(ctypes.byref(d), _ptr(dq_partial), _ptr(dq), _stream(stream)))
 
 
-def tri_attn_reduce_dbias(d, dbias_partial, dbias, stream=None):
+def tri_attn_reduce_dbias(d, dbias_partial, dbias, stream=None, bf16_partials=False):
+    """dbias from its partials; ``bf16_partials`` selects ``tri_attn_reduce_dbias_bf16p``."""
     _need(dbias, "dbias", torch.bfloat16, (d.B, d.H, d.N, d.N))
-    ws = workspace(d)
-    if dbias_partial.dtype != torch.float32 or dbias_partial.numel() < ws["dbias_partial_elems"] or not dbias_partial.is_contiguous():
-        raise ValueError("dbias_partial has the wrong dtype or size")
+    _need_partial(dbias_partial, "dbias_partial", _partial_dtype(bf16_partials), workspace(d)["dbias_partial_elems"])
     lib = _lib.load()
-    _lib.check("tri_attn_reduce_dbias", lib.tri_attn_reduce_dbias(ctypes.byref(d), _ptr(dbias_partial), _ptr(dbias),
-                                                                  _stream(stream)))
+    name = "tri_attn_reduce_dbias_bf16p" if bf16_partials else "tri_attn_reduce_dbias"
+    _lib.check(name, getattr(lib, name)(ctypes.byref(d), _ptr(dbias_partial), _ptr(dbias), _stream(stream)))
 
 
 # --------------------------------------------------------------------------- composite calls
@@ -142,26 +153,28 @@ def forward(q, k, v, bias, mask=None, scale=None, compensate=True):
     return o, o_res, lse
 
 
-def backward(q, k, v, bias, mask, scale, o, o_res, lse, d_o, workspace_buffers=None):
-    """Delta, key-tile backward and the two reductions.  Returns ``(dq, dk, dv, dbias)``."""
+def backward(q, k, v, bias, mask, scale, o, o_res, lse, d_o, workspace_buffers=None, bf16_partials=False):
+    """Delta, key-tile backward and the two reductions.  Returns ``(dq, dk, dv, dbias)``.
+    ``bf16_partials`` runs the bf16-partial variant (half the partial bytes)."""
     d = dims_of(q, scale)
     ws = workspace(d)
     delta = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     tri_attn_bwd_delta(d, o, o_res, d_o, delta)
     if workspace_buffers is None:
-        dq_part = torch.empty(ws["dq_partial_elems"], dtype=torch.float32, device=q.device)
-        db_part = torch.empty(ws["dbias_partial_elems"], dtype=torch.float32, device=q.device)
+        pdt = _partial_dtype(bf16_partials)
+        dq_part = torch.empty(ws["dq_partial_elems"], dtype=pdt, device=q.device)
+        db_part = torch.empty(ws["dbias_partial_elems"], dtype=pdt, device=q.device)
     else:
         dq_part, db_part = workspace_buffers
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    tri_attn_bwd(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv, dq_part, db_part)
+    tri_attn_bwd(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv, dq_part, db_part, bf16_partials=bf16_partials)
     dq = torch.empty_like(q)
     dbias = torch.empty_like(bias)
     # independent reductions; this order measured faster (the dQ reduction streams
     # better after the dbias reduction than straight after the backward)
-    tri_attn_reduce_dbias(d, db_part, dbias)
-    tri_attn_reduce_dq(d, dq_part, dq)
+    tri_attn_reduce_dbias(d, db_part, dbias, bf16_partials=bf16_partials)
+    tri_attn_reduce_dq(d, dq_part, dq, bf16_partials=bf16_partials)
     return dq, dk, dv, dbias
 
 

@@ -97,11 +97,15 @@ tri_attn_status tri_attn_bwd_delta(const tri_attn_dims* d, const tri_bf16* o,
   return launched(tri::launch_delta(a, (int)d->D, (hipStream_t)stream));
 }
 
-tri_attn_status tri_attn_bwd(const tri_attn_dims* d, const tri_bf16* q, const tri_bf16* k,
-                             const tri_bf16* v, const tri_bf16* bias, const float* mask,
-                             const tri_bf16* d_o, const float* lse, const float* delta,
-                             tri_bf16* dk, tri_bf16* dv, float* dq_partial, float* dbias_partial,
-                             tri_attn_stream stream) {
+}  // extern "C"
+
+namespace {
+
+tri_attn_status bwd_impl(const tri_attn_dims* d, const tri_bf16* q, const tri_bf16* k,
+                         const tri_bf16* v, const tri_bf16* bias, const float* mask,
+                         const tri_bf16* d_o, const float* lse, const float* delta, tri_bf16* dk,
+                         tri_bf16* dv, void* dq_partial, void* dbias_partial, int bf16_partials,
+                         tri_attn_stream stream) {
   tri_attn_status st = check_dims(d);
   if (st != TRI_ATTN_OK) return st;
   if (!q || !k || !v || !bias || !d_o || !lse || !delta || !dk || !dv || !dq_partial ||
@@ -115,6 +119,7 @@ tri_attn_status tri_attn_bwd(const tri_attn_dims* d, const tri_bf16* q, const tr
   a.q = q; a.k = k; a.v = v; a.bias = bias; a.mask = mask; a.d_o = d_o;
   a.lse = lse; a.delta = delta; a.dk = dk; a.dv = dv;
   a.dq_partial = dq_partial; a.dbias_partial = dbias_partial;
+  a.bf16_partials = bf16_partials;
   a.B = (int)d->B; a.N_o = (int)d->N_o; a.H = (int)d->H; a.N = (int)d->N;
   a.n_key_tiles = (int)n_key_tiles(d);
   a.n_groups = (int)n_groups(d);
@@ -124,30 +129,58 @@ tri_attn_status tri_attn_bwd(const tri_attn_dims* d, const tri_bf16* q, const tr
   return launched(tri::launch_bwd(a, (int)d->D, (hipStream_t)stream));
 }
 
-tri_attn_status tri_attn_reduce_dq(const tri_attn_dims* d, const float* dq_partial,
-                                   tri_bf16* dq, tri_attn_stream stream) {
+tri_attn_status reduce_impl(const tri_attn_dims* d, const void* partial, tri_bf16* out, bool dq,
+                            int bf16_partials, tri_attn_stream stream) {
   tri_attn_status st = check_dims(d);
   if (st != TRI_ATTN_OK) return st;
-  if (!dq_partial || !dq) return TRI_ATTN_ERR_NULL;
-  if (!aligned16(dq_partial) || !aligned16(dq)) return TRI_ATTN_ERR_ALIGN;
+  if (!partial || !out) return TRI_ATTN_ERR_NULL;
+  if (!aligned16(partial) || !aligned16(out)) return TRI_ATTN_ERR_ALIGN;
   tri::ReduceArgs a;
-  a.partial = dq_partial; a.out = dq;
-  a.elems = x_elems(d);
-  a.n_partials = (int)n_key_tiles(d);
+  a.partial = partial; a.out = out;
+  a.elems = dq ? x_elems(d) : y_elems(d);
+  a.n_partials = (int)(dq ? n_key_tiles(d) : n_groups(d));
+  a.bf16_partials = bf16_partials;
   return launched(tri::launch_reduce(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+tri_attn_status tri_attn_bwd(const tri_attn_dims* d, const tri_bf16* q, const tri_bf16* k,
+                             const tri_bf16* v, const tri_bf16* bias, const float* mask,
+                             const tri_bf16* d_o, const float* lse, const float* delta,
+                             tri_bf16* dk, tri_bf16* dv, float* dq_partial, float* dbias_partial,
+                             tri_attn_stream stream) {
+  return bwd_impl(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv, dq_partial, dbias_partial, 0, stream);
+}
+
+tri_attn_status tri_attn_bwd_bf16p(const tri_attn_dims* d, const tri_bf16* q, const tri_bf16* k,
+                                   const tri_bf16* v, const tri_bf16* bias, const float* mask,
+                                   const tri_bf16* d_o, const float* lse, const float* delta,
+                                   tri_bf16* dk, tri_bf16* dv, tri_bf16* dq_partial,
+                                   tri_bf16* dbias_partial, tri_attn_stream stream) {
+  return bwd_impl(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv, dq_partial, dbias_partial, 1, stream);
+}
+
+tri_attn_status tri_attn_reduce_dq(const tri_attn_dims* d, const float* dq_partial,
+                                   tri_bf16* dq, tri_attn_stream stream) {
+  return reduce_impl(d, dq_partial, dq, true, 0, stream);
 }
 
 tri_attn_status tri_attn_reduce_dbias(const tri_attn_dims* d, const float* dbias_partial,
                                       tri_bf16* dbias, tri_attn_stream stream) {
-  tri_attn_status st = check_dims(d);
-  if (st != TRI_ATTN_OK) return st;
-  if (!dbias_partial || !dbias) return TRI_ATTN_ERR_NULL;
-  if (!aligned16(dbias_partial) || !aligned16(dbias)) return TRI_ATTN_ERR_ALIGN;
-  tri::ReduceArgs a;
-  a.partial = dbias_partial; a.out = dbias;
-  a.elems = y_elems(d);
-  a.n_partials = (int)n_groups(d);
-  return launched(tri::launch_reduce(a, (hipStream_t)stream));
+  return reduce_impl(d, dbias_partial, dbias, false, 0, stream);
+}
+
+tri_attn_status tri_attn_reduce_dq_bf16p(const tri_attn_dims* d, const tri_bf16* dq_partial,
+                                         tri_bf16* dq, tri_attn_stream stream) {
+  return reduce_impl(d, dq_partial, dq, true, 1, stream);
+}
+
+tri_attn_status tri_attn_reduce_dbias_bf16p(const tri_attn_dims* d, const tri_bf16* dbias_partial,
+                                            tri_bf16* dbias, tri_attn_stream stream) {
+  return reduce_impl(d, dbias_partial, dbias, false, 1, stream);
 }
 
 }  // extern "C"

@@ -85,7 +85,8 @@ template <> struct Lay<16> {
 
 // LD: how the bias tile reaches LDS.  16: 16-byte direct loads (N % 8 == 0); 4: 4-byte
 // direct loads, one per 256-byte bias row (N even); 0: through registers (N odd).
-template <int D, bool MASK, int LD, int TK>
+// BP: dQ and dbias partials stored as bf16 (one RNE rounding each) instead of FP32.
+template <int D, bool MASK, int LD, bool BP, int TK>
 __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr bool VEC = LD != 0;   // direct global->LDS path
   constexpr int NW = TK / 16;     // waves; wave w owns keys 16w..16w+15 of the tile
@@ -397,10 +398,18 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         else dq0 = mfma_k32(ak[st], bs[st], dq0);
       }
       const int64_t prow = t * part_rows + srow(gg) + (int64_t)jj * TQ;
-      const uint32_t ext = __builtin_amdgcn_readfirstlane(store && gg < nsl ? (uint32_t)(N - jj * TQ) * D * 4 : 0u);
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dq_partial + prow * D, ext);
-      const uint32_t off = (uint32_t)((16 * qb + c) * D + 16 * db + 4 * g) * 4;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (dq0 + dq1) * scale), rs, off, 0, 0);
+      const f32x4 v = (dq0 + dq1) * scale;
+      if constexpr (BP) {   // bf16 partials: one RNE rounding, 8 bytes per lane
+        const uint32_t ext = __builtin_amdgcn_readfirstlane(store && gg < nsl ? (uint32_t)(N - jj * TQ) * D * 2 : 0u);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc((uint16_t*)a.dq_partial + prow * D, ext);
+        const uint32_t off = (uint32_t)((16 * qb + c) * D + 16 * db + 4 * g) * 2;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, rs, off, 0, 0);
+      } else {
+        const uint32_t ext = __builtin_amdgcn_readfirstlane(store && gg < nsl ? (uint32_t)(N - jj * TQ) * D * 4 : 0u);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc((float*)a.dq_partial + prow * D, ext);
+        const uint32_t off = (uint32_t)((16 * qb + c) * D + 16 * db + 4 * g) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
+      }
     }
   };
 
@@ -538,17 +547,23 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     if (kok) {
       // this group's dbias partial for (query tile j, key tile t); in the last query
       // tile rows past N go to an offset past the plane's extent and are dropped
+      const int64_t plane = (((int64_t)grp * a.B + b) * H + h) * N * N;
+      constexpr int EB = BP ? 2 : 4;         // bytes per partial element
       const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(a.dbias_partial + (((int64_t)grp * a.B + b) * H + h) * N * N, (uint32_t)N * N * 4);
+          BP ? make_rsrc((uint16_t*)a.dbias_partial + plane, (uint32_t)N * N * 2)
+             : make_rsrc((float*)a.dbias_partial + plane, (uint32_t)N * N * 4);
+      auto put = [&](float x, uint32_t voff, int soff) {
+        if constexpr (BP) __builtin_amdgcn_raw_buffer_store_b16(f_to_bf(x), rs, voff, soff, 0);
+        else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, voff, soff, 0);
+      };
       if ((j + 1) * TQ <= N) {
-        const uint32_t lane_off = (uint32_t)(8 * g * N + key) * 4;
+        const uint32_t lane_off = (uint32_t)(8 * g * N + key) * EB;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int rr = j * TQ + 32 * (qb >> 1) + 4 * (qb & 1) + i;   // row of group g = 0
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dbacc[qb][i]), rs, lane_off,
-                                                  (int)((uint32_t)rr * N * 4), 0);
+            put(dbacc[qb][i], lane_off, (int)((uint32_t)rr * N * EB));
           }
       } else {
 #pragma unroll
@@ -556,8 +571,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int q = j * TQ + 32 * (qb >> 1) + 8 * g + 4 * (qb & 1) + i;
-            const uint32_t off = q < N ? (uint32_t)(q * N + key) * 4 : 0xFFFFF000u;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dbacc[qb][i]), rs, off, 0, 0);
+            put(dbacc[qb][i], q < N ? (uint32_t)(q * N + key) * EB : 0xFFFFF000u, 0);
           }
       }
     }
@@ -605,7 +619,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   constexpr int TK = kBwdKeyTile;
   const int64_t nunit = (int64_t)a.B * a.n_groups * a.H;
   const int64_t nblk = 8 * ((nunit + 7) / 8) * a.n_key_tiles;
-  hipLaunchKernelGGL((bwd_kernel<D, MASK, LD, TK>), dim3((unsigned)nblk), dim3(TK * 4), 0, s, a);
+  if (a.bf16_partials)
+    hipLaunchKernelGGL((bwd_kernel<D, MASK, LD, true, TK>), dim3((unsigned)nblk), dim3(TK * 4), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_kernel<D, MASK, LD, false, TK>), dim3((unsigned)nblk), dim3(TK * 4), 0, s, a);
   return hipGetLastError();
 }
 

@@ -5,7 +5,8 @@
 // forms delta_hat = sum_d dO * (O + E) in FP32 from the BF16 output O and the
 // BF16 output residual E and writes it to HBM.
 // Reductions: Figure 7(d) and Figure 11(a) -- separate kernels add the
-// single-writer partials in ascending index order in FP32.
+// single-writer partials in ascending index order in FP32 (FP32 partials, or
+// bf16 partials as the pages' Table 2 sizes them).
 // All three are HBM-bound: coalesced 16-byte loads, no LDS.
 #include "common.h"
 #include "kernels.h"
@@ -51,10 +52,11 @@ template <int EPT>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   constexpr int NV = EPT / 4;     // 16-byte vectors per thread and partial
   constexpr int U = 8;            // partials per batch
+  const float* partial = static_cast<const float*>(a.partial);
   const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * EPT;
   if (i0 >= a.elems) return;
   if (i0 + EPT <= a.elems && (a.elems % 4) == 0) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(a.partial + i0);
+    const f32x4* src = reinterpret_cast<const f32x4*>(partial + i0);
     const int64_t pstride = a.elems / 4;        // in f32x4 units
     f32x4 acc[NV];
     for (int p = 0; p < a.n_partials; p += U) {
@@ -78,8 +80,46 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
       *reinterpret_cast<u32x2*>(a.out + i0 + 4 * v) = u32x2{pack_bf16(acc[v][0], acc[v][1]), pack_bf16(acc[v][2], acc[v][3])};
   } else {
     for (int64_t i = i0; i < i0 + EPT && i < a.elems; ++i) {
-      float acc = a.partial[i];
-      for (int p = 1; p < a.n_partials; ++p) acc += a.partial[(int64_t)p * a.elems + i];
+      float acc = partial[i];
+      for (int p = 1; p < a.n_partials; ++p) acc += partial[(int64_t)p * a.elems + i];
+      a.out[i] = f_to_bf(acc);
+    }
+  }
+}
+
+// The same sum over bf16 partials (each the RNE rounding of an FP32 partial): eight
+// elements per thread, one 16-byte load per partial, FP32 accumulation in ascending
+// partial order.
+__global__ __launch_bounds__(256) void reduce_bf16_kernel(ReduceArgs a) {
+  constexpr int U = 8;            // partials per batch
+  const uint16_t* partial = static_cast<const uint16_t*>(a.partial);
+  const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (i0 >= a.elems) return;
+  if (i0 + 8 <= a.elems && (a.elems % 8) == 0) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(partial + i0);
+    const int64_t pstride = a.elems / 8;        // in 16-byte units
+    float acc[8];
+    for (int p = 0; p < a.n_partials; p += U) {
+      u32x4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        x[u] = p + u < a.n_partials ? __builtin_nontemporal_load(src + (p + u) * pstride) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float y = (e & 1) ? bf_hi(x[u][e >> 1]) : bf_lo(x[u][e >> 1]);
+          if (p + u == 0) acc[e] = y;
+          else if (p + u < a.n_partials) acc[e] += y;
+        }
+      }
+    }
+    *reinterpret_cast<u32x4*>(a.out + i0) = u32x4{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
+                                                   pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7])};
+  } else {
+    for (int64_t i = i0; i < i0 + 8 && i < a.elems; ++i) {
+      float acc = bf_to_f(partial[i]);
+      for (int p = 1; p < a.n_partials; ++p) acc += bf_to_f(partial[(int64_t)p * a.elems + i]);
       a.out[i] = f_to_bf(acc);
     }
   }
@@ -101,6 +141,11 @@ hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t s) {
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
+  if (a.bf16_partials) {
+    const int64_t blocks = ((a.elems + 7) / 8 + 255) / 256;
+    hipLaunchKernelGGL(reduce_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   constexpr int EPT = 4;   // measured: 4 elements per thread streams faster than 8 for both reductions
   const int64_t threads = (a.elems + EPT - 1) / EPT;
   const int64_t blocks = (threads + 255) / 256;

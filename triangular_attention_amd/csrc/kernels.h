@@ -52,18 +52,20 @@ struct BwdArgs {
   const float* delta;
   uint16_t* dk;
   uint16_t* dv;
-  float* dq_partial;
-  float* dbias_partial;
+  void* dq_partial;      // FP32, or bf16 when bf16_partials
+  void* dbias_partial;
   int B, N_o, H, N;
   int n_key_tiles, n_groups;
   float scale;
+  int bf16_partials;     // 1: partials stored as bf16 (one RNE rounding each)
 };
 
 struct ReduceArgs {
-  const float* partial;
+  const void* partial;   // FP32, or bf16 when bf16_partials
   uint16_t* out;
   int64_t elems;    // elements of one partial (== elements of the output)
   int n_partials;
+  int bf16_partials;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int D, hipStream_t s);
