@@ -12,6 +12,10 @@ plain triangular attention (one probability evaluation, partial sums
 reordered), so the oracle is the plain definition written out in float64,
 not the tiled algorithm.
 
+``oracle.block_fp64`` extends it to the whole triangle-attention block
+(normalisation, projections, gate, output projection; starting and ending
+node), pinned by ``tests/test_oracle_block.py``.
+
 Every function here is pinned by ``tests/test_oracle.py`` against something
 other than itself (brute force, finite differences, a library special case,
 closed forms, invariants, or the indices of the worked example).
