@@ -139,3 +139,65 @@ def block_backward(z, gamma, beta, w_qkvg, w_b, w_o, dy, H, D, ending=False, eps
     return {"dz": _orient(dz, ending), "dw_qkvg": dw_qkvg, "dw_b": dw_b, "dw_o": dw_o,
             "dgamma": dgamma, "dbeta": dbeta, "do": do, "dg": dg, "dq": a["dq"],
             "dk": a["dk"], "dv": a["dv"], "dbias": a["dbias"], "y": f["y"]}
+
+
+def block_rows(z, gamma, beta, w_qkvg, w_b, w_o, dy, H, D, rows, ending=False, eps=1e-5):
+    """``y`` and ``dz`` of whole pair rows without the full backward (for full-size sampling).
+
+    ``rows = [(b, a), ...]`` name rows of the block's own orientation (for the ending node,
+    row a of the swapped tensors, i.e. column a of ``y`` and ``dz``).  Row a needs slice a
+    (its queries, keys, values and gate) and, for the bias gradient of pairs (a, .), query a
+    of every slice: ``dbias[h, a, :] = sum_o dS_o[h, a, :]`` (Figure 6, step 5).  Same
+    definitions and arithmetic as ``block_backward``; returns ``{"y": [R,N,C], "dz": [R,N,C]}``.
+    """
+    z = _orient(_f64(z), ending)
+    dy = _orient(_f64(dy), ending)
+    w_qkvg, w_b, w_o, gamma = _f64(w_qkvg), _f64(w_b), _f64(w_o), _f64(gamma)
+    HD = H * D
+    scale = 1.0 / math.sqrt(D)
+    zln, xhat, rstd = layer_norm(z, gamma, beta, eps)
+    wq, wk, wv, wg = (w_qkvg[i * HD:(i + 1) * HD] for i in range(4))
+    N = z.shape[1]
+    ys, dzs = [], []
+    cache = {}
+    for (b, a) in rows:
+        if b not in cache:
+            kb = (zln[b] @ wk.T).reshape(N, N, H, D).transpose(0, 2, 1, 3)     # [o,H,k,D]
+            vb = (zln[b] @ wv.T).reshape(N, N, H, D).transpose(0, 2, 1, 3)
+            biasb = (zln[b] @ w_b.T).transpose(2, 0, 1)                          # [H,q,k]
+            cache = {b: (kb, vb, biasb)}
+        kb, vb, biasb = cache[b]
+        # slice a: forward and backward of the attention
+        qa = (zln[b, a] @ wq.T).reshape(N, H, D).transpose(1, 0, 2)[None, None]  # [1,1,H,N,D]
+        ga = (zln[b, a] @ wg.T).reshape(N, H, D).transpose(1, 0, 2)[None, None]
+        ka, va = kb[a][None, None], vb[a][None, None]
+        oa, _ = attn_forward(qa, ka, va, biasb[None], None, scale)
+        sa = 1.0 / (1.0 + np.exp(-ga))
+        go = _pair_major(sa * oa)[0, 0]                                          # [N,HD]
+        ys.append(go @ w_o.T)
+        dgo = (dy[b, a] @ w_o).reshape(N, H, D).transpose(1, 0, 2)[None, None]    # [1,1,H,N,D]
+        do_a = dgo * sa
+        dg_a = dgo * oa * sa * (1.0 - sa)
+        g = attn_backward(qa, ka, va, biasb[None], None, scale, do_a)
+        # query a of every slice o: the bias-gradient row a
+        qc = (zln[b, :, a] @ wq.T).reshape(N, H, D)                               # [o,H,D]
+        gc = (zln[b, :, a] @ wg.T).reshape(N, H, D)
+        s = scale * np.einsum("ohd,ohkd->ohk", qc, kb) + biasb[None, :, a, :]
+        m = np.max(s, axis=-1, keepdims=True)
+        e = np.exp(s - m)
+        p = e / np.sum(e, axis=-1, keepdims=True)                                # [o,H,k]
+        oc = np.einsum("ohk,ohkd->ohd", p, vb)
+        sc = 1.0 / (1.0 + np.exp(-gc))
+        doc = (dy[b, :, a] @ w_o).reshape(N, H, D) * sc
+        dp = np.einsum("ohd,ohkd->ohk", doc, vb)
+        ds = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+        drow = np.zeros((H, N))
+        for o in range(N):                                                        # ascending o
+            drow = drow + ds[o]
+        dproj = np.concatenate([_pair_major(g["dq"])[0, 0], _pair_major(g["dk"])[0, 0],
+                                _pair_major(g["dv"])[0, 0], _pair_major(dg_a)[0, 0]], axis=-1)
+        dzln = dproj @ w_qkvg + drow.T @ w_b
+        dz, _, _ = layer_norm_backward(dzln, xhat[b, a], rstd[b, a], gamma)
+        dzs.append(dz)
+        del oc
+    return {"y": np.stack(ys), "dz": np.stack(dzs)}

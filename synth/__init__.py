@@ -158,3 +158,72 @@ def make_inputs_device(w: Workload, seed: int, device="cuda") -> dict:
         out["mask"] = torch.where(keep, torch.zeros((), device=device),
                                   torch.full((), MASK_VALUE, device=device)).float()
     return out
+
+
+# --------------------------------------------------------------------------- triangle-attention block
+
+
+@dataclasses.dataclass(frozen=True)
+class BlockWorkload:
+    """Inputs of the whole triangle-attention block: pair features Z [B, N, N, 128]."""
+    name: str
+    B: int
+    N: int
+    H: int
+    D: int
+    ending: bool = False
+    w_std: float = 0.02          # weights ~ N(0, w_std), rounded to bf16
+    ln_std: float = 0.0          # gamma = 1 + N(0, ln_std), beta = N(0, ln_std); 0: gamma 1, beta 0
+    description: str = ""
+
+    C_z = 128
+
+    @property
+    def pairs(self) -> int:
+        return self.B * self.N * self.N
+
+    @property
+    def flops_fwd_bwd(self) -> float:
+        """Attention (14 per score per head feature) + 3 x each projection's 2 * in * out per pair
+        (forward, input gradient, weight gradient)."""
+        F = self.H * self.D
+        attn = 14.0 * self.B * self.N * self.H * self.N * self.N * self.D
+        proj = 3 * 2.0 * self.pairs * self.C_z * (4 * F + self.H) + 3 * 2.0 * self.pairs * F * self.C_z
+        return attn + proj
+
+
+BLOCK_WORKLOADS = {
+    "block_n768": BlockWorkload(
+        "block_n768", 1, 768, 4, 32,
+        description="triangle-attention block, starting node: B=1 N=768 C_z=128 H=4 D=32; "
+                    "Z bf16 N(0,1), weights bf16 N(0,0.02), LayerNorm gamma 1 beta 0, dY bf16 N(0,1)"),
+    "block_n768_end": BlockWorkload(
+        "block_n768_end", 1, 768, 4, 32, ending=True,
+        description="triangle-attention block, ending node: B=1 N=768 C_z=128 H=4 D=32; "
+                    "Z bf16 N(0,1), weights bf16 N(0,0.02), LayerNorm gamma 1 beta 0, dY bf16 N(0,1)"),
+}
+
+
+def make_block_inputs(w: BlockWorkload, seed: int) -> dict:
+    """Seeded block inputs as CPU float32 tensors (bf16-representable where the kernels take bf16).
+
+    Draw order: Z, dY, w_qkvg, w_b, w_o, then gamma and beta (only when ``ln_std > 0``).
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    C, F = w.C_z, w.H * w.D
+    rb = lambda t: t.to(torch.bfloat16).to(torch.float32)
+    out = {
+        "z": rb(torch.randn((w.B, w.N, w.N, C), generator=g)),
+        "dy": rb(torch.randn((w.B, w.N, w.N, C), generator=g)),
+        "w_qkvg": rb(torch.randn((4 * F, C), generator=g) * w.w_std),
+        "w_b": rb(torch.randn((w.H, C), generator=g) * w.w_std),
+        "w_o": rb(torch.randn((C, F), generator=g) * w.w_std),
+    }
+    if w.ln_std > 0:
+        out["gamma"] = 1.0 + torch.randn(C, generator=g) * w.ln_std
+        out["beta"] = torch.randn(C, generator=g) * w.ln_std
+    else:
+        out["gamma"] = torch.ones(C)
+        out["beta"] = torch.zeros(C)
+    return out

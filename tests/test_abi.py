@@ -142,3 +142,67 @@ def test_workspace_ragged():
         assert ws["j_k"] == jk and ws["l"] == L
         assert ws["dq_partial_elems"] == jk * 2 * N_o * 3 * N * D
         assert ws["dbias_partial_elems"] == L * 2 * 3 * N * N
+
+
+# --------------------------------------------------------------------------- block ABI
+
+
+def _block_header_symbols():
+    txt = open(os.path.join(ROOT, "include", "tri_attn_block.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(tri_block_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_block_symbol(lib):
+    from triangular_attention_amd import _lib
+    syms = _block_header_symbols()
+    assert set(syms) == set(_lib.BLOCK_EXPORTS)
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def _bdims(**kw):
+    from triangular_attention_amd import _lib
+    base = dict(B=1, N=8, C_z=128, H=4, D=32, ending=0, eps=1e-5)
+    base.update(kw)
+    return _lib.BlockDims(base["B"], base["N"], base["C_z"], base["H"], base["D"], base["ending"], base["eps"])
+
+
+def _ln_proj(lib, d, **ptrs):
+    names = ("z", "gamma", "beta", "w_qkvg", "w_b", "q", "k", "v", "g", "bias", "ln_stats")
+    a = {n: P for n in names}
+    a.update(ptrs)
+    return lib.tri_block_ln_proj(None if d is None else ctypes.byref(d), *[a[n] for n in names], None)
+
+
+def test_block_validation_errors_before_launch(lib):
+    assert _ln_proj(lib, None) == 1
+    assert _ln_proj(lib, _bdims(C_z=64)) == 3
+    assert _ln_proj(lib, _bdims(H=2, D=32)) == 3          # H * D != 128
+    assert _ln_proj(lib, _bdims(H=2, D=64)) == 3          # D not 16 or 32
+    assert _ln_proj(lib, _bdims(N=0)) == 2
+    assert _ln_proj(lib, _bdims(eps=0.0)) == 2
+    assert _ln_proj(lib, _bdims(eps=float("nan"))) == 2
+    assert _ln_proj(lib, _bdims(ending=2)) == 2
+    assert _ln_proj(lib, _bdims(N=3000)) == 2             # pair tensor past 2^31 bytes
+    assert _ln_proj(lib, _bdims(), z=None) == 1
+    assert _ln_proj(lib, _bdims(), bias=MIS) == 4
+    d = _bdims(H=8, D=16, ending=1)
+    assert lib.tri_block_gate_out(ctypes.byref(d), P, P, P, None, None) == 1
+    assert lib.tri_block_gate_out_bwd(ctypes.byref(d), P, P, P, P, P, P, MIS, None) == 4
+    assert lib.tri_block_proj_bwd_dz(ctypes.byref(d), *([P] * 11), None, None) == 1
+    assert lib.tri_block_proj_bwd_dw(ctypes.byref(d), *([P] * 9), MIS, None) == 4
+    assert lib.tri_block_reduce_wgrad(ctypes.byref(d), *([P] * 7), None, None) == 1
+
+
+@pytest.mark.parametrize("B,N", [(1, 8), (1, 100), (2, 181), (1, 768)])
+def test_block_workspace_counts(lib, B, N):
+    """Partial buffers = workgroups of the fixed persistent grids (at most 256, 128 tile groups
+    for the weight gradients): pairs in tiles of 128 (output projection) and 64 (projections)."""
+    d = _bdims(B=B, N=N)
+    vals = [ctypes.c_int64() for _ in range(3)]
+    assert lib.tri_block_workspace(ctypes.byref(d), *[ctypes.byref(v) for v in vals]) == 0
+    pairs = B * N * N
+    assert vals[0].value == min(-(-pairs // 128), 256)
+    assert vals[1].value == min(-(-pairs // 64), 128)
+    assert vals[2].value == min(-(-pairs // 64), 256)

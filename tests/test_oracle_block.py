@@ -184,3 +184,19 @@ def test_symmetric_pairs_both_nodes():
     ys = _fwd(zs, p, H, D, False)
     ye = _fwd(zs, p, H, D, True)
     assert np.max(np.abs(ye - np.swapaxes(ys, 1, 2))) < 1e-13
+
+
+@pytest.mark.parametrize("ending", [False, True])
+def test_sampled_rows_match_full_backward(ending):
+    """The row-sampling form used at full size agrees with the full backward."""
+    H, D = 2, 3
+    z, dy, p = _case(B=2, N=7, Cz=5, H=H, D=D, seed=8)
+    full = _bwd(z, p, dy, H, D, ending)
+    rows = [(0, 0), (1, 3), (1, 6)]
+    r = blk.block_rows(z, p["gamma"], p["beta"], p["w_qkvg"], p["w_b"], p["w_o"], dy, H, D, rows,
+                       ending=ending)
+    for i, (b, a) in enumerate(rows):
+        yref = full["y"][b, :, a] if ending else full["y"][b, a]
+        dzref = full["dz"][b, :, a] if ending else full["dz"][b, a]
+        assert np.max(np.abs(r["y"][i] - yref)) < 1e-12
+        assert np.max(np.abs(r["dz"][i] - dzref)) < 1e-12

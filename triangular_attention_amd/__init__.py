@@ -4,9 +4,10 @@ The library ``libtri_attn.so`` (built from ``csrc/`` by ``build.py``) exports
 ``tri_attn_fwd``, ``tri_attn_bwd_delta``, ``tri_attn_bwd``,
 ``tri_attn_reduce_dq`` and ``tri_attn_reduce_dbias``; this package binds them
 with ctypes under the same names and offers ``triangular_attention`` as an
-autograd function.
+autograd function.  ``block`` binds the triangle-attention block around it
+(``tri_block_*``, include/tri_attn_block.h) and offers ``triangle_attention_block``.
 """
-from ._lib import EXPORTS, LIB_PATH, Dims, TriAttnError, load  # noqa: F401
+from ._lib import BLOCK_EXPORTS, EXPORTS, LIB_PATH, BlockDims, Dims, TriAttnError, load  # noqa: F401
 from .api import (  # noqa: F401
     backward,
     dims_of,
@@ -18,4 +19,11 @@ from .api import (  # noqa: F401
     tri_attn_reduce_dq,
     triangular_attention,
     workspace,
+)
+from .block import (  # noqa: F401
+    block_backward,
+    block_dims,
+    block_forward,
+    block_workspace,
+    triangle_attention_block,
 )

@@ -1,4 +1,5 @@
-"""ctypes binding of ``libtri_attn.so`` (the C ABI declared in include/tri_attn.h).
+"""ctypes binding of ``libtri_attn.so`` (the C ABI declared in include/tri_attn.h and
+include/tri_attn_block.h).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of the library.  Loading fails loudly when the library has not been
@@ -36,6 +37,17 @@ EXPORTS = (
     "tri_attn_version",
 )
 
+#: every symbol include/tri_attn_block.h declares
+BLOCK_EXPORTS = (
+    "tri_block_workspace",
+    "tri_block_ln_proj",
+    "tri_block_gate_out",
+    "tri_block_gate_out_bwd",
+    "tri_block_proj_bwd_dz",
+    "tri_block_proj_bwd_dw",
+    "tri_block_reduce_wgrad",
+)
+
 
 class Dims(ctypes.Structure):
     """Mirror of ``tri_attn_dims``."""
@@ -46,6 +58,19 @@ class Dims(ctypes.Structure):
         ("N", ctypes.c_int64),
         ("D", ctypes.c_int64),
         ("scale", ctypes.c_float),
+    ]
+
+
+class BlockDims(ctypes.Structure):
+    """Mirror of ``tri_block_dims``."""
+    _fields_ = [
+        ("B", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("C_z", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("D", ctypes.c_int64),
+        ("ending", ctypes.c_int32),
+        ("eps", ctypes.c_float),
     ]
 
 
@@ -81,6 +106,16 @@ def load() -> ctypes.CDLL:
         "tri_attn_reduce_dbias_bf16p": [dp, vp, vp, vp],
         "tri_attn_workspace": [dp, i64p, i64p, i64p, i64p, i64p, i64p],
     }
+    bp = ctypes.POINTER(BlockDims)
+    sig.update({
+        "tri_block_workspace": [bp, i64p, i64p, i64p],
+        "tri_block_ln_proj": [bp] + [vp] * 12,
+        "tri_block_gate_out": [bp] + [vp] * 5,
+        "tri_block_gate_out_bwd": [bp] + [vp] * 8,
+        "tri_block_proj_bwd_dz": [bp] + [vp] * 13,
+        "tri_block_proj_bwd_dw": [bp] + [vp] * 11,
+        "tri_block_reduce_wgrad": [bp] + [vp] * 9,
+    })
     for name, args in sig.items():
         f = getattr(lib, name)
         f.argtypes = args
