@@ -105,11 +105,12 @@ def cpu_baseline(w, seconds):
 
 def _short_kernel_name(name):
     name = name.replace("void ", "")
-    for k in ("fwd_kernel", "bwd_kernel", "delta_kernel", "reduce_kernel"):
-        if "tri::" + k in name:
-            return name.split("(")[0].replace("tri::", "")
     if "copy" in name.lower() or "elementwise" in name.lower():
         return "copy:" + name.split("(")[0][-60:]
+    if "tri::" in name:
+        # keep template arguments: cut the parameter list at the first "(" after the last "::"
+        base = name.replace("(anonymous namespace)::", "").replace("tri::", "")
+        return base.split("(")[0]
     return name.split("(")[0][-60:]
 
 
@@ -158,7 +159,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, copy_bytes, command, out):
     f_scale = copy_bytes / (max(fetch[ck]) * 1024.0)
     w_scale = copy_bytes / (max(write[ck]) * 1024.0)
     res = {"workload": workload, "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
-           "kernel_hash": kernel_hash(), "command": command, "kernels": {}}
+           "kernel_hash": kernel_hash(_hash_files(workload)), "command": command, "kernels": {}}
     for k in fetch:
         if k.startswith("copy:"):
             continue
@@ -200,6 +201,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload in synth.BLOCK_WORKLOADS:
+        bench_block(args, synth.BLOCK_WORKLOADS[args.workload], dev)
+        return
     w = synth.get(args.workload)
     x = synth.make_inputs(w, args.seed)
     q, k, v, do, bias = (x[n].to(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do", "bias"))
@@ -339,14 +343,225 @@ def main():
     print(json.dumps(out))
 
 
-def kernel_hash():
+BLOCK_KERNELS = ("ln_proj", "fwd", "gate_out", "gate_out_bwd", "delta", "bwd", "reduce_dbias", "reduce_dq",
+                 "proj_dz", "proj_dw", "reduce_wgrad")
+
+
+def algorithmic_block(bw, ws_attn, ws_blk):
+    """Algorithmic flops and minimum HBM bytes of one launch of each kernel of the block step."""
+    import synth
+    P, C, H = bw.pairs, bw.C_z, bw.H
+    F = bw.H * bw.D
+    wa = synth.Workload("attn", bw.B, bw.N, bw.N, bw.H, bw.D, 1.0 / (bw.D ** 0.5))
+    alg = algorithmic(wa, ws_attn["j_k"], ws_attn["l"])
+    Xb = 2 * P * F            # bytes of one [B,N,H,N,D] bf16 tensor
+    Zb = 2 * P * C            # bytes of Z / Y / dZ / dY
+    Yb = 2 * P * H            # bytes of bias / dbias
+    Wb = 2 * (4 * F + H) * C  # projection weights
+    nw, no, nl = ws_blk["n_w"], ws_blk["n_out"], ws_blk["n_ln"]
+    alg.update({
+        "ln_proj": {"flops": 2.0 * P * C * (4 * F + H), "bytes": Zb + 4 * Xb + Yb + 8 * P + Wb + 8 * C},
+        "gate_out": {"flops": 2.0 * P * F * C, "bytes": 2 * Xb + Zb + 2 * C * F},
+        "gate_out_bwd": {"flops": 4.0 * P * F * C, "bytes": Zb + 4 * Xb + 2 * C * F + 4 * no * C * F},
+        "proj_dz": {"flops": 2.0 * P * C * (4 * F + H), "bytes": 2 * Zb + 4 * Xb + Yb + 8 * P + Wb + 4 * nl * 2 * C},
+        "proj_dw": {"flops": 2.0 * P * C * (4 * F + H), "bytes": Zb + 4 * Xb + Yb + 8 * P + 4 * nw * (4 * F + H) * C},
+        "reduce_wgrad": {"flops": float(nw * (4 * F + H) * C + no * C * F + nl * 2 * C),
+                         "bytes": 4 * (nw * (4 * F + H) * C + no * C * F + nl * 2 * C)
+                                  + 4 * ((4 * F + H) * C + C * F + 2 * C)},
+    })
+    return alg
+
+
+def _roofline(alg, per, dom, traffic):
+    t_mfma = alg[dom]["flops"] / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = alg[dom]["bytes"] / (PEAK_HBM_GBS * 1e9)
+    ach_f = alg[dom]["flops"] / (per[dom] * 1e-3) / 1e12
+    ach_b = alg[dom]["bytes"] / (per[dom] * 1e-3) / 1e9
+    common = {"kernel": dom, "traffic": traffic, "avg_launch_ms": round(per[dom], 5),
+              "intensity_flop_per_byte": round(alg[dom]["flops"] / alg[dom]["bytes"], 1),
+              "mfma_frac": round(ach_f / PEAK_BF16_TFLOPS, 4), "hbm_frac": round(ach_b / PEAK_HBM_GBS, 4)}
+    if t_mfma >= t_hbm:
+        return {"bound": "mfma", "achieved": round(ach_f, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach_f / PEAK_BF16_TFLOPS, 4), **common}
+    return {"bound": "hbm", "achieved": round(ach_b, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(ach_b / PEAK_HBM_GBS, 4), **common}
+
+
+def _time_steps(calls, names, steps, warmup, stream):
+    """Whole-step time (HIP events around K steps) and per-kernel averages (events around each
+    launch, K more steps), all on the launch stream."""
+    import torch
+
+    def step():
+        for n in names:
+            calls[n]()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = ev0.elapsed_time(ev1) / steps
+    per = {n: 0.0 for n in names}
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    for s_ in range(steps):
+        evs[s_][0].record(stream)
+        for i, n in enumerate(names):
+            calls[n]()
+            evs[s_][i + 1].record(stream)
+    torch.cuda.synchronize()
+    for s_ in range(steps):
+        for i, n in enumerate(names):
+            per[n] += evs[s_][i].elapsed_time(evs[s_][i + 1]) / steps
+    return ms_step, per, t_wall
+
+
+def cpu_baseline_block(bw, seconds):
+    """The FP64 block oracle (as it stands) on a smaller crop of the same block (same C_z, H, D,
+    weights and distributions), sized to take about ``seconds``; rate in the metric's unit."""
+    import synth
+    from oracle import block_fp64 as blk
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+
+    def run(n):
+        w = synth.BlockWorkload("cpu", bw.B, n, bw.H, bw.D, ending=bw.ending, w_std=bw.w_std)
+        x = synth.make_block_inputs(w, 0)
+        a = [x[k].double().numpy() for k in ("z", "gamma", "beta", "w_qkvg", "w_b", "w_o")]
+        t0 = time.perf_counter()
+        blk.block_backward(*a, x["dy"].double().numpy(), bw.H, bw.D, ending=bw.ending)
+        return time.perf_counter() - t0, w.flops_fwd_bwd
+
+    n = 48
+    t, fl = run(n)
+    while t < seconds / 3 and n < bw.N:
+        n = min(bw.N, int(n * 1.5))
+        t, fl = run(n)
+    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole block fwd+bwd (FP64 numpy oracle, forward inside backward) at crop N={n} "
+                      f"(B={bw.B}, C_z=128, H={bw.H}, D={bw.D}, {'ending' if bw.ending else 'starting'} node), "
+                      f"seed 0; {t:.1f} s", "seconds": t, "crop": n}
+
+
+def bench_block(args, bw, dev):
+    """One step = the whole triangle-attention block, forward and backward (11 launches)."""
+    import torch
+
+    import synth
+    import triangular_attention_amd as ta
+    from triangular_attention_amd import block as tb
+
+    x = synth.make_block_inputs(bw, args.seed)
+    z, dy, w_qkvg, w_b, w_o = (x[n].to(torch.bfloat16).to(dev) for n in ("z", "dy", "w_qkvg", "w_b", "w_o"))
+    gamma, beta = x["gamma"].float().to(dev), x["beta"].float().to(dev)
+    B, N, H, D = bw.B, bw.N, bw.H, bw.D
+    F, C = H * D, bw.C_z
+    bd = tb.block_dims(B, N, H, D, bw.ending)
+    wsb = tb.block_workspace(bd)
+    hs = (B, N, H, N, D)
+    e = lambda shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=dev)
+    q, k, v, g, o, o_res, d_o, d_g, dq, dk, dv = (e(hs) for _ in range(11))
+    bias, dbias = e((B, H, N, N)), e((B, H, N, N))
+    stats = e((B, N, N, 2), torch.float32)
+    lse, delta = e((B, N, H, N), torch.float32), e((B, N, H, N), torch.float32)
+    y, dz = torch.empty_like(z), torch.empty_like(z)
+    ad = ta.dims_of(q, 1.0 / D ** 0.5)
+    wsa = ta.workspace(ad)
+    dqp, dbp = e(wsa["dq_partial_elems"], torch.float32), e(wsa["dbias_partial_elems"], torch.float32)
+    wo_part = e(wsb["n_out"] * C * F, torch.float32)
+    ln_part = e(wsb["n_ln"] * 2 * C, torch.float32)
+    w_part = e(wsb["n_w"] * (4 * F + H) * C, torch.float32)
+    dw_qkvg, dw_b, dw_o = e((4 * F, C), torch.float32), e((H, C), torch.float32), e((C, F), torch.float32)
+    dgamma, dbeta = e(C, torch.float32), e(C, torch.float32)
+    st = torch.cuda.current_stream()
+    calls = {
+        "ln_proj": lambda: tb.tri_block_ln_proj(bd, z, gamma, beta, w_qkvg, w_b, q, k, v, g, bias, stats, st),
+        "fwd": lambda: ta.tri_attn_fwd(ad, q, k, v, bias, None, o, o_res, lse, st),
+        "gate_out": lambda: tb.tri_block_gate_out(bd, o, g, w_o, y, st),
+        "gate_out_bwd": lambda: tb.tri_block_gate_out_bwd(bd, dy, o, g, w_o, d_o, d_g, wo_part, st),
+        "delta": lambda: ta.tri_attn_bwd_delta(ad, o, o_res, d_o, delta, st),
+        "bwd": lambda: ta.tri_attn_bwd(ad, q, k, v, bias, None, d_o, lse, delta, dk, dv, dqp, dbp, st),
+        "reduce_dbias": lambda: ta.tri_attn_reduce_dbias(ad, dbp, dbias, st),
+        "reduce_dq": lambda: ta.tri_attn_reduce_dq(ad, dqp, dq, st),
+        "proj_dz": lambda: tb.tri_block_proj_bwd_dz(bd, z, stats, gamma, w_qkvg, w_b, dq, dk, dv, d_g, dbias,
+                                                    dz, ln_part, st),
+        "proj_dw": lambda: tb.tri_block_proj_bwd_dw(bd, z, stats, gamma, beta, dq, dk, dv, d_g, dbias, w_part, st),
+        "reduce_wgrad": lambda: tb.tri_block_reduce_wgrad(bd, w_part, wo_part, ln_part, dw_qkvg, dw_b, dw_o,
+                                                          dgamma, dbeta, st),
+    }
+    ms_step, per, t_wall = _time_steps(calls, BLOCK_KERNELS, args.steps, args.warmup, st)
+    alg = algorithmic_block(bw, wsa, wsb)
+    kernels = {n: {"ms": round(per[n], 5),
+                   "tflops": round(alg[n]["flops"] / (per[n] * 1e-3) / 1e12, 2),
+                   "alg_gbs": round(alg[n]["bytes"] / (per[n] * 1e-3) / 1e9, 1)} for n in BLOCK_KERNELS}
+    dom = max(BLOCK_KERNELS, key=lambda n: per[n])
+    traffic, traffic_all = None, None
+    if os.path.exists(args.traffic):
+        try:
+            tr = json.load(open(args.traffic)).get(bw.name, {})
+            if tr.get("kernel_hash") == kernel_hash(None):
+                traffic_all = tr["kernels"]
+                for kname, val in traffic_all.items():
+                    if kname.startswith(dom + "_kernel"):
+                        traffic = round(val["bytes_per_launch"])
+        except Exception:
+            traffic = None
+    value = bw.flops_fwd_bwd / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": "tri-attn fwd+bwd TFLOP/s & ms at N=768,H=4,D=32 bf16; % bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": bw.name, "B": B, "N": N, "C_z": C, "H": H, "D": D, "ending": bw.ending,
+                   "w_std": bw.w_std, "flops_per_step": bw.flops_fwd_bwd,
+                   "attention_flops": 14.0 * B * N * H * N * N * D, "description": bw.description},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels": kernels,
+        "roofline": _roofline(alg, per, dom, traffic),
+        "wall_s_timed": round(t_wall, 4),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if traffic_all is not None:
+        out["traffic_bytes_per_launch"] = {kk: round(vv["bytes_per_launch"]) for kk, vv in traffic_all.items()}
+    if args.copy_bytes > 0:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = args.copy_bytes
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_block(bw, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+def _hash_files(workload):
+    return None if workload.startswith("block") else ATTN_SOURCES
+
+
+ATTN_SOURCES = ("common.h", "kernels.h", "api.hip", "fwd.hip", "bwd.hip", "delta_reduce.hip")
+BLOCK_SOURCES = ("common.h", "block_kernels.h", "block_api.hip", "block.hip")
+
+
+def kernel_hash(files=ATTN_SOURCES):
     """Hash of the kernel sources without comments and whitespace: stored traffic counters
-    are valid only for the same code (a comment edit keeps them)."""
+    are valid only for the same code (a comment edit keeps them).  ``files`` = the sources of
+    the measured kernels (None: every source)."""
     import hashlib
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "triangular_attention_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(os.listdir(csrc)) if files is None else sorted(files):
         txt = open(os.path.join(csrc, f), encoding="utf-8").read()
         txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
         txt = re.sub(r"//[^\n]*", " ", txt)

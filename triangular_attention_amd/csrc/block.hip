@@ -687,11 +687,22 @@ __global__ __launch_bounds__(NT) void proj_dw_kernel(BlkProjBwdArgs a) {
 }
 
 // Fixed-order sum of partial buffers: out[e] = sum_{i = 0..n-1} partial[i][e], ascending i.
+// Loads are issued 16 partials at a time (independent), the adds stay in ascending order.
 __global__ __launch_bounds__(256) void blk_reduce_kernel(BlkReduceArgs a) {
+  constexpr int U = 16;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= a.elems) return;
+  const float* p = a.partial + e;
   float s = 0.f;
-  for (int i = 0; i < a.n; ++i) s += a.partial[(size_t)i * a.elems + e];
+  int i = 0;
+  for (; i + U <= a.n; i += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + (size_t)(i + u) * a.elems);
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += v[u];
+  }
+  for (; i < a.n; ++i) s += p[(size_t)i * a.elems];
   if (e < a.split) a.out0[e] = s;
   else a.out1[e - a.split] = s;
 }
