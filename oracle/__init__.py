@@ -14,7 +14,8 @@ not the tiled algorithm.
 
 ``oracle.block_fp64`` extends it to the whole triangle-attention block
 (normalisation, projections, gate, output projection; starting and ending
-node), pinned by ``tests/test_oracle_block.py``.
+node), pinned by ``tests/test_oracle_block.py``; ``oracle.trimul_fp64`` is the triangle
+multiplicative update (Figure 12), pinned by ``tests/test_oracle_trimul.py``.
 
 Every function here is pinned by ``tests/test_oracle.py`` against something
 other than itself (brute force, finite differences, a library special case,
