@@ -227,3 +227,72 @@ def make_block_inputs(w: BlockWorkload, seed: int) -> dict:
         out["gamma"] = torch.ones(C)
         out["beta"] = torch.zeros(C)
     return out
+
+
+# --------------------------------------------------------------------------- triangle multiplicative update
+
+
+@dataclasses.dataclass(frozen=True)
+class TrimulWorkload:
+    """Inputs of the triangle multiplicative update: pair features Z [B, N, N, 128], c channels."""
+    name: str
+    B: int
+    N: int
+    c: int
+    incoming: bool = False
+    w_std: float = 0.02          # weights ~ N(0, w_std), rounded to bf16
+    ln_std: float = 0.0          # gammas = 1 + N(0, ln_std), betas = N(0, ln_std); 0: 1 and 0
+    description: str = ""
+
+    C_z = 128
+
+    @property
+    def pairs(self) -> int:
+        return self.B * self.N * self.N
+
+    @property
+    def flops_fwd_bwd(self) -> float:
+        """3 x (input projections + per-channel contraction + output projection): forward, input
+        gradient and weight (or second operand) gradient of each product."""
+        P, C, c = self.pairs, self.C_z, self.c
+        return 3 * (2.0 * P * C * (4 * c + C) + 2.0 * self.B * c * self.N ** 3 + 2.0 * P * c * C)
+
+
+def _tm(name, N, c, inc):
+    side = "incoming" if inc else "outgoing"
+    return TrimulWorkload(name, 1, N, c, incoming=inc,
+                          description=f"triangle multiplicative update, {side}: B=1 N={N} C_z=128 c={c}; "
+                                      f"Z bf16 N(0,1), weights bf16 N(0,0.02), LayerNorm gammas 1 betas 0, "
+                                      f"dout bf16 N(0,1)")
+
+
+#: The pages' update sizes (Table 10): crops 384/640/768 with 128 channels, 384/640 with 64.
+TRIMUL_WORKLOADS = {w.name: w for w in [
+    _tm(f"trimul_n{n}_c{c}_{'in' if inc else 'out'}", n, c, inc)
+    for (n, c) in ((384, 128), (640, 128), (768, 128), (384, 64), (640, 64)) for inc in (False, True)]}
+
+
+def make_trimul_inputs(w: TrimulWorkload, seed: int) -> dict:
+    """Seeded inputs as CPU float32 tensors (bf16-representable where the kernels take bf16).
+
+    Draw order: Z, dout, w_in, w_o, then gamma, beta, gamma_o, beta_o (only when ``ln_std > 0``).
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    C, c = w.C_z, w.c
+    rb = lambda t: t.to(torch.bfloat16).to(torch.float32)
+    out = {
+        "z": rb(torch.randn((w.B, w.N, w.N, C), generator=g)),
+        "dout": rb(torch.randn((w.B, w.N, w.N, C), generator=g)),
+        "w_in": rb(torch.randn((4 * c + C, C), generator=g) * w.w_std),
+        "w_o": rb(torch.randn((C, c), generator=g) * w.w_std),
+    }
+    if w.ln_std > 0:
+        out["gamma"] = 1.0 + torch.randn(C, generator=g) * w.ln_std
+        out["beta"] = torch.randn(C, generator=g) * w.ln_std
+        out["gamma_o"] = 1.0 + torch.randn(c, generator=g) * w.ln_std
+        out["beta_o"] = torch.randn(c, generator=g) * w.ln_std
+    else:
+        out["gamma"], out["beta"] = torch.ones(C), torch.zeros(C)
+        out["gamma_o"], out["beta_o"] = torch.ones(c), torch.zeros(c)
+    return out

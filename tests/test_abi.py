@@ -206,3 +206,61 @@ def test_block_workspace_counts(lib, B, N):
     assert vals[0].value == min(-(-pairs // 128), 256)
     assert vals[1].value == min(-(-pairs // 64), 128)
     assert vals[2].value == min(-(-pairs // 64), 256)
+
+
+# --------------------------------------------------------------------------- triangle multiplication ABI
+
+
+def test_library_exports_every_trimul_symbol(lib):
+    from triangular_attention_amd import _lib
+    txt = open(os.path.join(ROOT, "include", "tri_mul.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    syms = sorted(set(re.findall(r"\b(tri_mul_[a-z0-9_]+)\s*\(", txt)))
+    assert set(syms) == set(_lib.TRIMUL_EXPORTS)
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def _mdims(**kw):
+    from triangular_attention_amd import _lib
+    base = dict(B=1, N=16, C_z=128, c=128, incoming=0, eps=1e-5)
+    base.update(kw)
+    return _lib.MulDims(base["B"], base["N"], base["C_z"], base["c"], base["incoming"], base["eps"])
+
+
+def test_trimul_validation_errors_before_launch(lib):
+    f = lambda d, **p: lib.tri_mul_in_fwd(None if d is None else ctypes.byref(d),
+                                          *[p.get(n, P) for n in ("z", "g1", "b1", "w", "a", "b", "g", "s")], None)
+    assert f(None) == 1
+    assert f(_mdims(c=32)) == 3
+    assert f(_mdims(C_z=64)) == 3
+    assert f(_mdims(N=12)) == 2            # N % 8 != 0
+    assert f(_mdims(N=0)) == 2
+    assert f(_mdims(eps=-1.0)) == 2
+    assert f(_mdims(incoming=3)) == 2
+    assert f(_mdims(N=1456, c=128)) == 2   # dproj past 2^31 bytes
+    assert f(_mdims(), z=None) == 1
+    assert f(_mdims(), a=MIS) == 4
+    d = _mdims(c=64, incoming=1)
+    assert lib.tri_mul_contract(ctypes.byref(d), P, P, None, None) == 1
+    assert lib.tri_mul_contract_bwd(ctypes.byref(d), P, P, P, P, MIS, None) == 4
+    assert lib.tri_mul_out_bwd(ctypes.byref(d), *([P] * 10), None, None) == 1
+    assert lib.tri_mul_in_bwd_dw(ctypes.byref(d), *([P] * 6), MIS, None) == 4
+    assert lib.tri_mul_reduce_wgrad(ctypes.byref(d), *([P] * 9), None, None) == 1
+
+
+@pytest.mark.parametrize("B,N,c", [(1, 8, 64), (1, 136, 128), (2, 384, 64), (1, 768, 128)])
+def test_trimul_workspace_counts(lib, B, N, c):
+    """Partial buffers = workgroups of the fixed persistent grids: tiles of 64 (output backward) and
+    32 (input dZ) pairs capped at 256, tile groups of 64 pairs capped at 8 * floor(256 / (8 * rows / 128))
+    for the input weight gradient (rows = 4c + 128), and two wave halves per workgroup for the output
+    normalisation when c = 64."""
+    d = _mdims(B=B, N=N, c=c)
+    vals = [ctypes.c_int64() for _ in range(4)]
+    assert lib.tri_mul_workspace(ctypes.byref(d), *[ctypes.byref(v) for v in vals]) == 0
+    pairs = B * N * N
+    splits = (4 * c + 128) // 128
+    assert vals[0].value == min(-(-pairs // 64), 8 * (256 // (8 * splits)))
+    assert vals[1].value == min(-(-pairs // 64), 256)
+    assert vals[2].value == min(-(-pairs // 32), 256)
+    assert vals[3].value == vals[1].value * (128 // c)

@@ -5,9 +5,11 @@ The library ``libtri_attn.so`` (built from ``csrc/`` by ``build.py``) exports
 ``tri_attn_reduce_dq`` and ``tri_attn_reduce_dbias``; this package binds them
 with ctypes under the same names and offers ``triangular_attention`` as an
 autograd function.  ``block`` binds the triangle-attention block around it
-(``tri_block_*``, include/tri_attn_block.h) and offers ``triangle_attention_block``.
+(``tri_block_*``, include/tri_attn_block.h) and offers ``triangle_attention_block``;
+``trimul`` binds the triangle multiplicative update (``tri_mul_*``, include/tri_mul.h) and
+offers ``triangle_multiplication``.
 """
-from ._lib import BLOCK_EXPORTS, EXPORTS, LIB_PATH, BlockDims, Dims, TriAttnError, load  # noqa: F401
+from ._lib import BLOCK_EXPORTS, EXPORTS, LIB_PATH, TRIMUL_EXPORTS, BlockDims, Dims, MulDims, TriAttnError, load  # noqa: F401
 from .api import (  # noqa: F401
     backward,
     dims_of,
@@ -26,4 +28,11 @@ from .block import (  # noqa: F401
     block_forward,
     block_workspace,
     triangle_attention_block,
+)
+from .trimul import (  # noqa: F401
+    mul_dims,
+    mul_workspace,
+    triangle_multiplication,
+    trimul_backward,
+    trimul_forward,
 )

@@ -1,5 +1,5 @@
-"""ctypes binding of ``libtri_attn.so`` (the C ABI declared in include/tri_attn.h and
-include/tri_attn_block.h).
+"""ctypes binding of ``libtri_attn.so`` (the C ABI declared in include/tri_attn.h,
+include/tri_attn_block.h and include/tri_mul.h).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of the library.  Loading fails loudly when the library has not been
@@ -48,6 +48,20 @@ BLOCK_EXPORTS = (
     "tri_block_reduce_wgrad",
 )
 
+#: every symbol include/tri_mul.h declares
+TRIMUL_EXPORTS = (
+    "tri_mul_workspace",
+    "tri_mul_in_fwd",
+    "tri_mul_contract",
+    "tri_mul_out_fwd",
+    "tri_mul_out_bwd",
+    "tri_mul_contract_bwd",
+    "tri_mul_in_bwd",
+    "tri_mul_in_bwd_dz",
+    "tri_mul_in_bwd_dw",
+    "tri_mul_reduce_wgrad",
+)
+
 
 class Dims(ctypes.Structure):
     """Mirror of ``tri_attn_dims``."""
@@ -70,6 +84,18 @@ class BlockDims(ctypes.Structure):
         ("H", ctypes.c_int64),
         ("D", ctypes.c_int64),
         ("ending", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+    ]
+
+
+class MulDims(ctypes.Structure):
+    """Mirror of ``tri_mul_dims``."""
+    _fields_ = [
+        ("B", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("C_z", ctypes.c_int64),
+        ("c", ctypes.c_int64),
+        ("incoming", ctypes.c_int32),
         ("eps", ctypes.c_float),
     ]
 
@@ -115,6 +141,19 @@ def load() -> ctypes.CDLL:
         "tri_block_proj_bwd_dz": [bp] + [vp] * 13,
         "tri_block_proj_bwd_dw": [bp] + [vp] * 11,
         "tri_block_reduce_wgrad": [bp] + [vp] * 9,
+    })
+    mp = ctypes.POINTER(MulDims)
+    sig.update({
+        "tri_mul_workspace": [mp, i64p, i64p, i64p, i64p],
+        "tri_mul_in_fwd": [mp] + [vp] * 9,
+        "tri_mul_contract": [mp] + [vp] * 4,
+        "tri_mul_out_fwd": [mp] + [vp] * 8,
+        "tri_mul_out_bwd": [mp] + [vp] * 12,
+        "tri_mul_contract_bwd": [mp] + [vp] * 6,
+        "tri_mul_in_bwd": [mp] + [vp] * 9,
+        "tri_mul_in_bwd_dz": [mp] + [vp] * 9,
+        "tri_mul_in_bwd_dw": [mp] + [vp] * 8,
+        "tri_mul_reduce_wgrad": [mp] + [vp] * 11,
     })
     for name, args in sig.items():
         f = getattr(lib, name)

@@ -16,7 +16,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libtri_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "delta_reduce.hip", "block.hip", "block_api.hip"]
+SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "delta_reduce.hip", "block.hip", "block_api.hip", "trimul.hip",
+           "trimul_api.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed FP32 instructions (v_pk_*_f32)

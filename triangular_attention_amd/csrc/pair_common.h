@@ -1,0 +1,78 @@
+// Device helpers shared by the pair-feature kernels (triangle-attention block and triangle
+// multiplicative update): swizzled LDS tiles of 128-element rows, 16-lane DPP sums, the
+// LayerNorm forms every kernel must share bit for bit, pair indexing and bf16 packing.
+#pragma once
+#include "common.h"
+
+namespace tri {
+namespace pair {
+
+// Chunk swizzle of a 256-byte row: rows r and r' of any aligned group of 16 get
+// different XOR masks; within an aligned group of 4 rows the masks differ in bits 1-2 only.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1); }
+// element offset of logical 16-byte chunk j (0..15) of row r in a [rows][128] bf16 tile
+__device__ __forceinline__ int toff(int r, int j) { return r * 128 + ((j ^ swz(r)) << 3); }
+
+// Transposing read of an 8-slot MFMA operand from a swizzled [rows][128] tile:
+// the lane receives column col0 + (lane & 15) of rows row0 + 0..7.
+__device__ __forceinline__ u32x4 tr8_swz(const uint16_t* tile, int row0, int col0, int lane) {
+  const int kk = (lane & 15) >> 2, a = lane & 3;
+  const int col = col0 + 4 * a, j = col >> 3, half = (col >> 2) & 1;
+  const int r0 = row0 + kk, r1 = r0 + 4;
+  return ds_read_tr8_at(tile, toff(r0, j) + 4 * half, toff(r1, j) + 4 * half);
+}
+
+// Sum over the 16 lanes of a row with DPP; every lane ends with the same value.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);   // row_half_mirror
+  x += dpp_mov<0x140>(x);   // row_mirror
+  return x;
+}
+
+// The normalised feature exactly as every kernel forms it (forward and backward
+// must agree bit for bit): xhat = (z - mean) * rstd, zln = xhat * gamma + beta (one FMA).
+__device__ __forceinline__ float ln_xhat(float z, float mean, float rstd) { return (z - mean) * rstd; }
+__device__ __forceinline__ float ln_out(float xh, float gm, float bt) { return __builtin_fmaf(xh, gm, bt); }
+__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+
+struct PairIx { int b, x, y; };
+__device__ __forceinline__ PairIx pair_ix(int r, int N) {
+  const int nn = N * N;
+  PairIx p;
+  p.b = r / nn;
+  const int rem = r - p.b * nn;
+  p.x = rem / N;
+  p.y = rem - p.x * N;
+  return p;
+}
+// Element offset of the pair's 128-feature row in Z / dZ / Y / dY.
+__device__ __forceinline__ int zrow(const PairIx& p, int N, int ending) {
+  return ((p.b * N + (ending ? p.y : p.x)) * N + (ending ? p.x : p.y)) * 128;
+}
+// Element offset of (pair, head h, feature d) in a [B, N, H, N, D] tensor.
+template <int H, int D>
+__device__ __forceinline__ int hm_off(const PairIx& p, int N, int h, int d) {
+  return ((p.b * N + p.x) * H + h) * N * D + p.y * D + d;
+}
+
+__device__ __forceinline__ void unpack8(u32x4 v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f[2 * i] = bf_lo(v[i]); f[2 * i + 1] = bf_hi(v[i]); }
+}
+__device__ __forceinline__ u32x4 pack8(const float* f) {
+  return u32x4{pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7])};
+}
+__device__ __forceinline__ void st_lds16(uint16_t* tile, int off, u32x4 v) {
+  *reinterpret_cast<u32x4*>(tile + off) = v;
+}
+__device__ __forceinline__ u32x4 ld_lds16(const uint16_t* tile, int off) {
+  return *reinterpret_cast<const u32x4*>(tile + off);
+}
+
+}  // namespace pair
+}  // namespace tri
