@@ -204,6 +204,9 @@ def main():
     if args.workload in synth.BLOCK_WORKLOADS:
         bench_block(args, synth.BLOCK_WORKLOADS[args.workload], dev)
         return
+    if args.workload in synth.TRIMUL_WORKLOADS:
+        bench_trimul(args, synth.TRIMUL_WORKLOADS[args.workload], dev)
+        return
     w = synth.get(args.workload)
     x = synth.make_inputs(w, args.seed)
     q, k, v, do, bias = (x[n].to(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do", "bias"))
@@ -545,8 +548,126 @@ def bench_block(args, bw, dev):
     print(json.dumps(out))
 
 
+TRIMUL_KERNELS = ("in_fwd", "contract", "out_fwd", "out_bwd", "contract_bwd", "in_bwd", "in_dz", "in_dw",
+                  "reduce_wgrad")
+
+
+def algorithmic_trimul(tw, ws):
+    """Algorithmic flops and minimum HBM bytes of one launch of each call of the update step."""
+    P, C, c, B, N = tw.pairs, tw.C_z, tw.c, tw.B, tw.N
+    Zb, Cb = 2 * P * C, 2 * P * c          # one pair-major [.., 128] / channel-major [B, c, N, N] bf16 tensor
+    Wb = 2 * (4 * c + C) * C
+    gemm = 2.0 * B * c * N ** 3
+    nw, no, nl, nlo = ws["n_w"], ws["n_out"], ws["n_ln"], ws["n_lno"]
+    return {
+        "in_fwd": {"flops": 2.0 * P * C * (4 * c + C), "bytes": Zb + 2 * Cb + Zb + 8 * P + Wb},
+        "contract": {"flops": gemm, "bytes": 3 * Cb},
+        "out_fwd": {"flops": 2.0 * P * c * C, "bytes": Cb + 2 * Zb + 8 * P + 2 * C * c},
+        "out_bwd": {"flops": 6.0 * P * c * C, "bytes": 2 * Zb + Cb + 8 * P + Cb + Zb + 4 * (no * C * c + nlo * 2 * c)},
+        "contract_bwd": {"flops": 2 * gemm, "bytes": 5 * Cb},
+        "in_bwd": {"flops": 2.0 * P * C * 4 * c, "bytes": Zb + 8 * P + 2 * Cb + 2 * P * 4 * c + Wb},
+        "in_dz": {"flops": 2.0 * P * (4 * c + C) * C, "bytes": 2 * P * 4 * c + Zb + Zb + 8 * P + Zb + Wb},
+        "in_dw": {"flops": 2.0 * P * (4 * c + C) * C, "bytes": 2 * P * 4 * c + Zb + Zb + 8 * P + 4 * nw * (4 * c + C) * C},
+        "reduce_wgrad": {"flops": float(nw * (4 * c + C) * C + no * C * c + nl * 2 * C + nlo * 2 * c),
+                         "bytes": 4 * (nw * (4 * c + C) * C + no * C * c + nl * 2 * C + nlo * 2 * c)},
+    }
+
+
+def cpu_baseline_trimul(tw, seconds):
+    """The FP64 oracle (as it stands) on a smaller crop of the same update, sized to take about
+    ``seconds``; rate in the metric's unit."""
+    import synth
+    from oracle import trimul_fp64 as tmo
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+
+    def run(n):
+        w = synth.TrimulWorkload("cpu", tw.B, n, tw.c, incoming=tw.incoming, w_std=tw.w_std)
+        x = synth.make_trimul_inputs(w, 0)
+        a = [x[k].double().numpy() for k in ("z", "gamma", "beta", "w_in", "gamma_o", "beta_o", "w_o")]
+        t0 = time.perf_counter()
+        tmo.trimul_backward(*a, x["dout"].double().numpy(), tw.c, incoming=tw.incoming)
+        return time.perf_counter() - t0, w.flops_fwd_bwd
+
+    n = 64
+    t, fl = run(n)
+    while t < seconds / 3 and n < tw.N:
+        n = min(tw.N, int(n * 1.5) // 8 * 8)
+        t, fl = run(n)
+    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole update fwd+bwd (FP64 numpy oracle, forward inside backward) at crop N={n} "
+                      f"(B={tw.B}, C_z=128, c={tw.c}, {'incoming' if tw.incoming else 'outgoing'}), seed 0; "
+                      f"{t:.1f} s", "seconds": t, "crop": n}
+
+
+def bench_trimul(args, tw, dev):
+    """One step = the triangle multiplicative update, forward and backward (9 calls, 10 launches
+    plus the reductions)."""
+    import torch
+
+    import synth
+    from triangular_attention_amd import trimul as tmb
+
+    x = synth.make_trimul_inputs(tw, args.seed)
+    z, dout, w_in, w_o = (x[n].to(torch.bfloat16).to(dev) for n in ("z", "dout", "w_in", "w_o"))
+    gamma, beta, gamma_o, beta_o = (x[n].float().to(dev) for n in ("gamma", "beta", "gamma_o", "beta_o"))
+    B, N, c, C = tw.B, tw.N, tw.c, tw.C_z
+    d = tmb.mul_dims(B, N, c, tw.incoming)
+    ws = tmb.mul_workspace(d)
+    e = lambda shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=dev)
+    cs = (B, c, N, N)
+    a, b, xx, dx, da, db = (e(cs) for _ in range(6))
+    g, out, dg, dz = (torch.empty_like(z) for _ in range(4))
+    stats, stats_o = e((B * N * N, 2), torch.float32), e((B * N * N, 2), torch.float32)
+    dproj = e((B * N * N, 4 * c))
+    wo_part, lno_part = e(ws["n_out"] * C * c, torch.float32), e(ws["n_lno"] * 2 * c, torch.float32)
+    ln_part, w_part = e(ws["n_ln"] * 2 * C, torch.float32), e(ws["n_w"] * (4 * c + C) * C, torch.float32)
+    dw_in, dw_o = e((4 * c + C, C), torch.float32), e((C, c), torch.float32)
+    dgm, dbt, dgo, dbo = e(C, torch.float32), e(C, torch.float32), e(c, torch.float32), e(c, torch.float32)
+    st = torch.cuda.current_stream()
+    calls = {
+        "in_fwd": lambda: tmb.tri_mul_in_fwd(d, z, gamma, beta, w_in, a, b, g, stats, st),
+        "contract": lambda: tmb.tri_mul_contract(d, a, b, xx, st),
+        "out_fwd": lambda: tmb.tri_mul_out_fwd(d, xx, g, gamma_o, beta_o, w_o, out, stats_o, st),
+        "out_bwd": lambda: tmb.tri_mul_out_bwd(d, dout, xx, g, stats_o, gamma_o, beta_o, w_o, dx, dg, wo_part,
+                                               lno_part, st),
+        "contract_bwd": lambda: tmb.tri_mul_contract_bwd(d, dx, a, b, da, db, st),
+        "in_bwd": lambda: tmb.tri_mul_in_bwd(d, z, stats, gamma, beta, w_in, da, db, dproj, st),
+        "in_dz": lambda: tmb.tri_mul_in_bwd_dz(d, z, stats, gamma, w_in, dproj, dg, dz, ln_part, st),
+        "in_dw": lambda: tmb.tri_mul_in_bwd_dw(d, z, stats, gamma, beta, dproj, dg, w_part, st),
+        "reduce_wgrad": lambda: tmb.tri_mul_reduce_wgrad(d, w_part, wo_part, ln_part, lno_part, dw_in, dw_o, dgm,
+                                                         dbt, dgo, dbo, st),
+    }
+    ms_step, per, t_wall = _time_steps(calls, TRIMUL_KERNELS, args.steps, args.warmup, st)
+    alg = algorithmic_trimul(tw, ws)
+    kernels = {n: {"ms": round(per[n], 5),
+                   "tflops": round(alg[n]["flops"] / (per[n] * 1e-3) / 1e12, 2),
+                   "alg_gbs": round(alg[n]["bytes"] / (per[n] * 1e-3) / 1e9, 1)} for n in TRIMUL_KERNELS}
+    dom = max(TRIMUL_KERNELS, key=lambda n: per[n])
+    value = tw.flops_fwd_bwd / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "tri-attn fwd+bwd TFLOP/s & ms at N=768,H=4,D=32 bf16; % bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": tw.name, "B": B, "N": N, "C_z": C, "c": c, "incoming": tw.incoming,
+                   "w_std": tw.w_std, "flops_per_step": tw.flops_fwd_bwd, "description": tw.description},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels": kernels,
+        "roofline": _roofline(alg, per, dom, None),
+        "wall_s_timed": round(t_wall, 4),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_trimul(tw, args.cpu_seconds)
+    print(json.dumps(res))
+
+
 def _hash_files(workload):
-    return None if workload.startswith("block") else ATTN_SOURCES
+    return None if workload.startswith(("block", "trimul")) else ATTN_SOURCES
 
 
 ATTN_SOURCES = ("common.h", "kernels.h", "api.hip", "fwd.hip", "bwd.hip", "delta_reduce.hip")
