@@ -404,13 +404,21 @@ __global__ __launch_bounds__(NT) void tm_out_fwd_kernel(TmOutArgs a) {
   for (int s = 0; s < CH / 32; ++s) wo[s] = ld_global<u32x4>(a.w_o + (16 * w + c) * CH + 32 * s + 8 * g);
   const int pp = t & (TP - 1), qq = t >> 7;    // statistics: pair pp, channel quarter qq
 
+  const uint32_t gbytes = (uint32_t)total * C * 2;
+  const auto gr = make_rsrc(a.g, gbytes);
   u32x4 xv[NLD];
+  u32x2 gv[TP / 16];        // this lane's gate logits of the tile (4 features of one pair per block)
   auto load = [&](int tile) {
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
       const int q = t + NT * k, ch = q >> 4, seg = q & 15;
       const int r0 = tile * TP + 8 * seg;
       xv[k] = buf_ld16(xr, r0 < total ? (uint32_t)cm_off(r0, ch, nn, CH) * 2 : xbytes);
+    }
+#pragma unroll
+    for (int pb = 0; pb < TP / 16; ++pb) {
+      const int r = tile * TP + 16 * pb + c;
+      gv[pb] = buf_ld8(gr, r < total ? (uint32_t)(r * C + 16 * w + 4 * g) * 2 : gbytes);
     }
   };
   if ((int)blockIdx.x < ntiles) load(blockIdx.x);
@@ -421,6 +429,9 @@ __global__ __launch_bounds__(NT) void tm_out_fwd_kernel(TmOutArgs a) {
       const int q = t + NT * k;
       st_lds16(sX, coff(q >> 4, 8 * (q & 15)), xv[k]);
     }
+    u32x2 gc[TP / 16];
+#pragma unroll
+    for (int pb = 0; pb < TP / 16; ++pb) gc[pb] = gv[pb];
     const int nt = tile + gridDim.x;
     if (nt < ntiles) load(nt);
     lds_barrier();
@@ -450,7 +461,7 @@ __global__ __launch_bounds__(NT) void tm_out_fwd_kernel(TmOutArgs a) {
     const int rp = tile * TP + pp;
     if (qq == 0 && rp < total) *reinterpret_cast<f32x2*>(a.stats_o + 2 * (size_t)rp) = f32x2{mean, rstd};
     lds_barrier();
-#pragma unroll 2
+#pragma unroll
     for (int pb = 0; pb < TP / 16; ++pb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -458,7 +469,7 @@ __global__ __launch_bounds__(NT) void tm_out_fwd_kernel(TmOutArgs a) {
       const int r = tile * TP + 16 * pb + c;
       if (r < total) {
         const size_t o = (size_t)r * C + 16 * w + 4 * g;
-        const u32x2 gl = *reinterpret_cast<const u32x2*>(a.g + o);
+        const u32x2 gl = gc[pb];
         const float gf[4] = {bf_lo(gl[0]), bf_hi(gl[0]), bf_lo(gl[1]), bf_hi(gl[1])};
         float ov[4];
 #pragma unroll
@@ -477,8 +488,6 @@ template <int CH>
 __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
   constexpr int TP = kTmTileOutBwd;
   constexpr int SEGS = TP / 8;                          // 16-byte chunks per channel row of a tile
-  constexpr int NQQ = NT / TP;                          // channel groups in the elementwise phase
-  constexpr int NQ = CH / NQQ;
   constexpr int NLD = CH * TP / 8 / NT;
   constexpr int NPB = CH == 128 ? TP / 16 : TP / 32;   // pair blocks of a wave in the dx product
   constexpr int KC = NPB < 4 ? NPB : 4;                 // pair blocks per chunk of the dx phase
@@ -495,8 +504,9 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
   const int N = a.s.N, nn = N * N;
   const int total = a.s.B * nn;
   const int ntiles = (total + TP - 1) / TP;
-  const uint32_t xbytes = (uint32_t)total * CH * 2;
+  const uint32_t xbytes = (uint32_t)total * CH * 2, pbytes = (uint32_t)total * C * 2;
   const auto xr = make_rsrc(a.x, xbytes);
+  const auto dr = make_rsrc(a.dout, pbytes), gr = make_rsrc(a.g, pbytes);
   for (int i = t; i < CH; i += NT) { sGam[i] = a.gamma_o[i]; sBet[i] = a.beta_o[i]; }
   u32x4 wo[CH / 32];
 #pragma unroll
@@ -522,7 +532,9 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
   for (int i = 0; i < 4; ++i) { gm[i] = a.gamma_o[chb * 16 + 4 * g + i]; dgam[i] = 0.f; dbet[i] = 0.f; }
   const int pp = t & (TP - 1), qq = t / TP;
 
+  const auto sr = make_rsrc(a.stats_o, (uint32_t)total * 8);
   u32x4 xv[NLD];
+  f32x2 stv;                // statistics of this thread's pair pp
   auto load = [&](int tile) {
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
@@ -530,6 +542,8 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
       const int r0 = tile * TP + 8 * seg;
       xv[k] = buf_ld16(xr, r0 < total ? (uint32_t)cm_off(r0, ch, nn, CH) * 2 : xbytes);
     }
+    const int rp = tile * TP + pp;
+    stv = __builtin_bit_cast(f32x2, buf_ld8(sr, rp < total ? (uint32_t)rp * 8 : (uint32_t)total * 8));
   };
   if ((int)blockIdx.x < ntiles) load(blockIdx.x);
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -539,17 +553,35 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
       const int q = t + NT * k;
       st_lds16(sX, coff(q / SEGS, 8 * (q % SEGS)), xv[k]);
     }
+    const f32x2 s = stv;
     const int nt = tile + gridDim.x;
     if (nt < ntiles) load(nt);
+    // this lane's incoming gradient and gate logits (4 features of one pair per block), in
+    // flight while the tile is normalised
+    u32x2 dlv[TP / 16], glv[TP / 16];
+#pragma unroll
+    for (int pb = 0; pb < TP / 16; ++pb) {
+      const int r = tile * TP + 16 * pb + c;
+      const uint32_t o = r < total ? (uint32_t)(r * C + 16 * w + 4 * g) * 2 : pbytes;
+      dlv[pb] = buf_ld8(dr, o);
+      glv[pb] = buf_ld8(gr, o);
+    }
     {
-      const int rp = tile * TP + pp;
-      const f32x2 s = rp < total ? *reinterpret_cast<const f32x2*>(a.stats_o + 2 * (size_t)rp) : f32x2{0.f, 0.f};
       if (qq == 0) { sSt[pp][0] = s[0]; sSt[pp][1] = s[1]; }
       lds_barrier();
+      // LN(x) 8 pairs of one channel at a time (the chunks this thread staged)
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) {
-        const int ch = qq * NQ + j, o = coff(ch, pp);
-        sXL[o] = f_to_bf(ln_out(ln_xhat(bf_to_f(sX[o]), s[0], s[1]), sGam[ch], sBet[ch]));
+      for (int k = 0; k < NLD; ++k) {
+        const int q = t + NT * k, ch = q / SEGS, seg = q % SEGS;
+        float xf[8], y[8];
+        unpack8(ld_lds16(sX, coff(ch, 8 * seg)), xf);
+        const float gmv = sGam[ch], btv = sBet[ch];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int pq = 8 * seg + e;
+          y[e] = ln_out(ln_xhat(xf[e], sSt[pq][0], sSt[pq][1]), gmv, btv);
+        }
+        st_lds16(sXL, coff(ch, 8 * seg), pack8(y));
       }
     }
     lds_barrier();
@@ -561,11 +593,7 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
       for (int s = 0; s < CH / 32; ++s) acc = mfma_k32(wo[s], tr8_pad(sXL, 32 * s + 8 * g, 16 * pb, lane), acc);
       const int rl = 16 * pb + c, r = tile * TP + rl;
       const size_t o = (size_t)(r < total ? r : 0) * C + 16 * w + 4 * g;
-      u32x2 dl = {0u, 0u}, gl = {0u, 0u};
-      if (r < total) {
-        dl = *reinterpret_cast<const u32x2*>(a.dout + o);
-        gl = *reinterpret_cast<const u32x2*>(a.g + o);
-      }
+      const u32x2 dl = dlv[pb], gl = glv[pb];
       const float df[4] = {bf_lo(dl[0]), bf_hi(dl[0]), bf_lo(dl[1]), bf_hi(dl[1])};
       const float gf[4] = {bf_lo(gl[0]), bf_hi(gl[0]), bf_lo(gl[1]), bf_hi(gl[1])};
       float dp[4], dg[4];
