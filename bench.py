@@ -390,6 +390,43 @@ def _roofline(alg, per, dom, traffic):
             "unit": "GB/s", "frac": round(ach_b / PEAK_HBM_GBS, 4), **common}
 
 
+# kernel-name prefix of each call of the triangle-multiplication step (for measured traffic)
+TRIMUL_LAUNCH_KERNELS = {"in_fwd": "tm_in_fwd_kernel", "contract": "tm_gemm_kernel<false, false",
+                         "out_fwd": "tm_out_fwd_kernel", "out_bwd": "tm_out_bwd_kernel",
+                         "in_bwd": "tm_in_bwd_kernel", "in_dz": "tm_in_dz_kernel", "in_dw": "tm_in_dw_kernel"}
+
+
+def _traffic_lookup(path, workload, dom, prefix):
+    """Measured bytes per launch of the dominant call's kernel from the counter summary, if it was
+    taken on the current sources."""
+    if not os.path.exists(path):
+        return None, None
+    try:
+        tr = json.load(open(path)).get(workload, {})
+        if tr.get("kernel_hash") != kernel_hash(None):
+            return None, None
+        allk = tr["kernels"]
+        for kname, val in allk.items():
+            if kname.startswith(prefix):
+                return round(val["bytes_per_launch"]), allk
+        return None, allk
+    except Exception:
+        return None, None
+
+
+def _copy_calibration(args, dev, out):
+    """A plain device copy of --copy-bytes (3 times): the reference for the byte counters."""
+    import torch
+    if args.copy_bytes > 0:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = args.copy_bytes
+
+
 def _time_steps(calls, names, steps, warmup, stream):
     """Whole-step time (HIP events around K steps) and per-kernel averages (events around each
     launch, K more steps), all on the launch stream."""
@@ -647,6 +684,7 @@ def bench_trimul(args, tw, dev):
                    "tflops": round(alg[n]["flops"] / (per[n] * 1e-3) / 1e12, 2),
                    "alg_gbs": round(alg[n]["bytes"] / (per[n] * 1e-3) / 1e9, 1)} for n in TRIMUL_KERNELS}
     dom = max(TRIMUL_KERNELS, key=lambda n: per[n])
+    traffic, traffic_all = _traffic_lookup(args.traffic, tw.name, dom, TRIMUL_LAUNCH_KERNELS.get(dom, dom))
     value = tw.flops_fwd_bwd / (ms_step * 1e-3) / 1e12
     res = {
         "metric": "tri-attn fwd+bwd TFLOP/s & ms at N=768,H=4,D=32 bf16; % bf16 MFMA peak",
@@ -657,10 +695,13 @@ def bench_trimul(args, tw, dev):
                    "w_std": tw.w_std, "flops_per_step": tw.flops_fwd_bwd, "description": tw.description},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kernels": kernels,
-        "roofline": _roofline(alg, per, dom, None),
+        "roofline": _roofline(alg, per, dom, traffic),
         "wall_s_timed": round(t_wall, 4),
         "gpu": torch.cuda.get_device_name(0),
     }
+    if traffic_all is not None:
+        res["traffic_bytes_per_launch"] = {kk: round(vv["bytes_per_launch"]) for kk, vv in traffic_all.items()}
+    _copy_calibration(args, dev, res)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_trimul(tw, args.cpu_seconds)
     print(json.dumps(res))
