@@ -143,17 +143,19 @@ __global__ __launch_bounds__(NT) void tm_in_fwd_kernel(TmInArgs a) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int kind = item_kind<CH>(it, w), cb = item_cb<CH>(it, w);
+        // pairs as rows: lane (g, c) gets pairs 16pb + 4g + 0..3 of channel cb*16 + c, written
+        // to the [channel][pair] tile as one 8-byte word
         f32x4 av = {0.f, 0.f, 0.f, 0.f}, ag = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          av = mfma_k32(wv[it][s], bf[s], av);
-          ag = mfma_k32(wq[it][s], bf[s], ag);
+          av = mfma_k32(bf[s], wv[it][s], av);
+          ag = mfma_k32(bf[s], wq[it][s], ag);
         }
+        float ab[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ch = cb * 16 + 4 * g + i;
-          sAB[kind][coff(ch, rl)] = f_to_bf(sigm(ag[i]) * av[i]);
-        }
+        for (int i = 0; i < 4; ++i) ab[i] = sigm(ag[i]) * av[i];
+        *reinterpret_cast<u32x2*>(&sAB[kind][coff(cb * 16 + c, 16 * pb + 4 * g)]) =
+            u32x2{pack_bf16(ab[0], ab[1]), pack_bf16(ab[2], ab[3])};
       }
       f32x4 go = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
