@@ -64,7 +64,9 @@ typedef enum {
   TRI_ATTN_ERR_LAUNCH = 5
 } tri_attn_status;
 
-/* Problem dimensions.  D must be 16 or 32; B, N_o, H >= 1; 1 <= N <= 32767; scale finite. */
+/* Problem dimensions.  D must be 16, 32 or 64 (the method is measured at 16 and 32;
+ * 64 is a wider head run by the same kernels); B, N_o, H >= 1; 1 <= N <= 32767; scale
+ * finite. */
 typedef struct {
   int64_t B, N_o, H, N, D;
   float scale;
@@ -145,8 +147,10 @@ tri_attn_status tri_attn_reduce_dbias_bf16p(const tri_attn_dims* d, const tri_bf
 
 /*
  * Partial-buffer sizes for these dimensions (elements, FP32), the number of
- * key tiles J_K and of outer groups L, and the key-tile / group sizes used.
- * Any output pointer may be NULL.  Host-only arithmetic; no device access.
+ * key tiles J_K and of outer groups L, and the key-tile / group sizes used
+ * (key tile 128; group G = 4 for D = 32, 6 for D = 16 with N even and 4 with N
+ * odd, 2 for D = 64).  Any output pointer may be NULL.  Host-only arithmetic; no
+ * device access.
  */
 tri_attn_status tri_attn_workspace(const tri_attn_dims* d, int64_t* dq_partial_elems,
                                    int64_t* dbias_partial_elems, int64_t* j_k, int64_t* l,

@@ -71,6 +71,14 @@ WORKLOADS = {
     "n768_d32_mask": _w("n768_d32_mask", 768, 4, 32, 1.0 / math.sqrt(32), mask_p=0.1,
                         description="B=1 N_o=N=768 H=4 D=32 bf16 N(0,1), bias N(0,1), "
                                     "per-slice key mask Bernoulli(0.1) additive -1e9, scale 1/sqrt(32)"),
+    # the largest crop of the pages' memory table (Table 2), which they size but do not time
+    "n1024_d32_mask": _w("n1024_d32_mask", 1024, 4, 32, 1.0 / math.sqrt(32), mask_p=0.1,
+                         description="B=1 N_o=N=1024 H=4 D=32 bf16 N(0,1), bias N(0,1), "
+                                     "per-slice key mask Bernoulli(0.1) additive -1e9, scale 1/sqrt(32)"),
+    # a wider head than the pages measure: the crop-768 workload with D = 64
+    "n768_d64_mask": _w("n768_d64_mask", 768, 4, 64, 1.0 / 8.0, mask_p=0.1,
+                        description="B=1 N_o=N=768 H=4 D=64 bf16 N(0,1), bias N(0,1), "
+                                    "per-slice key mask Bernoulli(0.1) additive -1e9, scale 1/sqrt(64)"),
 }
 
 #: The six-shape sweep: crops {384, 640, 768} x head dims {16, 32}, H=4, no mask.

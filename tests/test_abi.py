@@ -57,7 +57,7 @@ def _fwd(lib, d, **ptrs):
 
 def test_validation_errors_before_launch(lib):
     assert _fwd(lib, None) == 1
-    assert _fwd(lib, _dims(D=64)) == 3
+    assert _fwd(lib, _dims(D=128)) == 3
     assert _fwd(lib, _dims(D=8)) == 3
     assert _fwd(lib, _dims(N=0)) == 2
     assert _fwd(lib, _dims(N=32768, N_o=1)) == 2     # 4*N*N must fit in 32 bits
@@ -82,7 +82,7 @@ def test_validation_errors_before_launch(lib):
     # the bf16-partial variant validates like the FP32 calls
     assert lib.tri_attn_bwd_bf16p(ctypes.byref(d), P, P, P, P, None, P, P, P, P, P, P, None, None) == 1
     assert lib.tri_attn_bwd_bf16p(ctypes.byref(d), P, P, P, P, None, P, P, P, P, P, MIS, P, None) == 4
-    assert lib.tri_attn_bwd_bf16p(ctypes.byref(_dims(D=64)), P, P, P, P, None, P, P, P, P, P, P, P, None) == 3
+    assert lib.tri_attn_bwd_bf16p(ctypes.byref(_dims(D=128)), P, P, P, P, None, P, P, P, P, P, P, P, None) == 3
     assert lib.tri_attn_reduce_dq_bf16p(ctypes.byref(d), None, P, None) == 1
     assert lib.tri_attn_reduce_dq_bf16p(ctypes.byref(d), MIS, P, None) == 4
     assert lib.tri_attn_reduce_dbias_bf16p(ctypes.byref(_dims(N=0)), P, P, None) == 2
@@ -91,7 +91,7 @@ def test_validation_errors_before_launch(lib):
 def test_python_binding_raises(lib):
     from triangular_attention_amd import _lib
     with pytest.raises(_lib.TriAttnError):
-        _lib.check("tri_attn_fwd", _fwd(lib, _dims(D=64)))
+        _lib.check("tri_attn_fwd", _fwd(lib, _dims(D=128)))
 
 
 def _golden_table2():
@@ -132,10 +132,11 @@ def test_workspace_matches_memory_table():
 
 def test_workspace_ragged():
     """Partial counts for ragged shapes.  The outer group is 4 slices except on the direct-load
-    path with D = 16 (N even), where the smaller accumulators leave room for 6."""
+    path with D = 16 (N even), where the smaller accumulators leave room for 6, and 2 slices for
+    D = 64, whose accumulators are twice as large."""
     from triangular_attention_amd import api
     for (N_o, N, D, G) in ((10, 65, 16, 4), (10, 64, 16, 6), (10, 66, 16, 6), (10, 64, 32, 4), (13, 200, 16, 6),
-                           (13, 201, 32, 4)):
+                           (13, 201, 32, 4), (13, 200, 64, 2), (13, 201, 64, 2)):
         ws = api.workspace(_dims(B=2, N_o=N_o, H=3, N=N, D=D))
         jk, L = -(-N // ws["key_tile"]), -(-N_o // G)
         assert ws["outer_group"] == G and ws["key_tile"] == 128

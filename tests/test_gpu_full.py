@@ -1,4 +1,5 @@
-"""GPU checks at the full workload sizes (crops 384/640/768, D 16/32, H=4):
+"""GPU checks at the full workload sizes (crops 384/640/768, D 16/32, H=4; the crop-768
+workload with D = 64 and the crop-1024 one with D = 32):
 
 * parity on sampled outputs the oracle computes one by one (whole slices for
   O, dQ, dK, dV; whole rows of dbias, which sum over every slice);
@@ -19,7 +20,7 @@ from gpu_util import np64, require_gpu, to_dev
 pytestmark = pytest.mark.gpu
 
 TOL_O, TOL_G = 5e-3, 1.5e-2
-FULL = ["n384_d32", "n640_d16", "n768_d32_mask"]
+FULL = ["n384_d32", "n640_d16", "n768_d32_mask", "n768_d64_mask", "n1024_d32_mask"]
 
 
 def _poisoned_call(ta, dev, scale, compensate=True):

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 TOL_O = 5e-3
 TOL_G = 1.5e-2
 
-# (N_o, N, H, D, mask_p, bias_std, B): several tiles, ragged tails, both D, masks,
+# (N_o, N, H, D, mask_p, bias_std, B): several tiles, ragged tails, every D, masks,
 # all three bias-load paths (16-byte direct loads for N % 8 == 0, 4-byte direct loads
 # for other even N, registers for odd N) and incomplete last outer groups
 CASES = [
@@ -38,6 +38,11 @@ CASES = [
     (9, 67, 2, 32, 0.2, 1.0, 1),       # odd N, masked, D = 32
     (3, 63, 1, 16, 0.1, 1.0, 3),       # odd N, D = 16, one head, B = 3
     (5, 50, 2, 16, 0.0, 1.0, 1),       # D = 16, no mask, N % 8 == 2 (4-byte loads)
+    (6, 72, 2, 64, 0.1, 1.0, 1),       # D = 64, masked, N % 8 == 0, three groups of 2 slices
+    (5, 100, 2, 64, 0.3, 2.0, 1),      # D = 64, N % 8 == 4 (4-byte loads), last group of 1 slice
+    (4, 200, 1, 64, 0.0, 1.0, 1),      # D = 64, 2 key tiles, 7 query tiles of 32 (stage cycle wraps)
+    (7, 33, 2, 64, 0.2, 1.0, 2),       # D = 64, odd N (register path), B = 2
+    (3, 130, 2, 64, 0.0, 1.0, 1),      # D = 64, no mask, N % 8 == 2, ragged key tile
 ]
 
 
@@ -192,7 +197,7 @@ def test_python_validation_on_device():
 
 
 @pytest.mark.parametrize("case", [(9, 72, 3, 32, 0.1, 1.0, 1), (5, 100, 2, 32, 0.3, 2.0, 2), (8, 96, 2, 16, 0.15, 1.0, 1),
-                                  (9, 67, 2, 32, 0.2, 1.0, 1)], ids=_id)
+                                  (9, 67, 2, 32, 0.2, 1.0, 1), (6, 72, 2, 64, 0.1, 1.0, 1)], ids=_id)
 def test_bf16_partials_variant_matches_oracle(case):
     """The bf16-partial variant (tri_attn_bwd_bf16p and its reductions): every gradient within
     the tolerance of the oracle, dK and dV bitwise equal to the FP32-partial path (they never

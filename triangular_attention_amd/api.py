@@ -196,7 +196,7 @@ class _TriAttn(torch.autograd.Function):
 def triangular_attention(q, k, v, bias, mask=None, scale=None, compensate=True):
     """Triangular attention with a pair bias shared by every outer slice.
 
-    q, k, v: ``[B, N_o, H, N, D]`` bf16 (D in {16, 32}); bias ``[B, H, N, N]`` bf16;
+    q, k, v: ``[B, N_o, H, N, D]`` bf16 (D in {16, 32, 64}); bias ``[B, H, N, N]`` bf16;
     mask: ``[B, N_o, N]`` additive float32, or a bool tensor (True = keep), or None.
     Returns O ``[B, N_o, H, N, D]`` bf16; differentiable in q, k, v and bias.
     """

@@ -16,7 +16,7 @@ tri_attn_status check_dims(const tri_attn_dims* d) {
   if (!d) return TRI_ATTN_ERR_NULL;
   if (d->B < 1 || d->N_o < 1 || d->H < 1 || d->N < 1 || d->D < 1) return TRI_ATTN_ERR_SHAPE;
   if (!std::isfinite(d->scale)) return TRI_ATTN_ERR_SHAPE;
-  if (d->D != 16 && d->D != 32) return TRI_ATTN_ERR_UNSUPPORTED;
+  if (d->D != 16 && d->D != 32 && d->D != 64) return TRI_ATTN_ERR_UNSUPPORTED;
   // 32-bit index limits of the kernels: every per-tensor row count fits in int32 and
   // the byte size of one FP32 N x N plane (4*N*N) fits in uint32
   const int64_t rows = d->B * d->N_o * d->H * d->N;
@@ -43,7 +43,7 @@ const char* tri_attn_status_string(tri_attn_status s) {
     case TRI_ATTN_OK: return "ok";
     case TRI_ATTN_ERR_NULL: return "null pointer argument";
     case TRI_ATTN_ERR_SHAPE: return "invalid dimensions or scale";
-    case TRI_ATTN_ERR_UNSUPPORTED: return "unsupported head dimension (D must be 16 or 32)";
+    case TRI_ATTN_ERR_UNSUPPORTED: return "unsupported head dimension (D must be 16, 32 or 64)";
     case TRI_ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
     case TRI_ATTN_ERR_LAUNCH: return "kernel launch failed";
   }

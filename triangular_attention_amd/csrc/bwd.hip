@@ -83,6 +83,47 @@ template <> struct Lay<16> {
   static constexpr int kSlotsPerRow = 3;     // two data chunks and one padding chunk
 };
 
+// D = 64: unpadded 128-byte rows of eight 16-byte chunks, the chunk index XORed with a
+// row-dependent value.  Per half-wave, the score-product row reads touch four rows of
+// equal (row mod 4) at two chunks each (Q / dO: rows differing in bits 3-4; K / V: bits
+// 2-3) and the transposing reads four rows of equal parity at two chunks each (bits 1
+// and 3); the XOR values below give every such set eight distinct 16-byte positions
+// (and distinct 8-byte units for the transposing reads).
+template <> struct Lay<64> {
+  static constexpr int kRowElems = 64;
+  static constexpr int kKVRowElems = 64;
+  __device__ static __forceinline__ int swq(int row) {
+    return (((row >> 1) & 1) * 2) ^ (((row >> 3) & 1) * 5) ^ (((row >> 4) & 1) * 4);
+  }
+  __device__ static __forceinline__ int swk(int row) {
+    return (((row >> 1) & 1) * 2) ^ (((row >> 2) & 1) * 4) ^ (((row >> 3) & 1) * 5);
+  }
+  __device__ static __forceinline__ int q(int row, int col) {
+    return row * 64 + ((((col >> 3) ^ swq(row)) & 7) << 3) + (col & 7);
+  }
+  __device__ static __forceinline__ int k(int row, int col) {
+    return row * 64 + ((((col >> 3) ^ swk(row)) & 7) << 3) + (col & 7);
+  }
+  __device__ static __forceinline__ int v(int row, int col) { return k(row, col); }
+  __device__ static __forceinline__ int q_src_chunk(int row, int pchunk) { return (pchunk ^ swq(row)) & 7; }
+  static constexpr int kSlotsPerRow = 8;
+};
+
+// One lane's contraction operand (DOp<D>::T) from an LDS tile: D / 4 elements from
+// column col of row row; with D = 64 its two 16-byte chunks sit at their own swizzled
+// positions.
+template <int D, typename F>
+__device__ __forceinline__ typename DOp<D>::T ld_op(const uint16_t* t, int row, int col, F at) {
+  if constexpr (D == 64) {
+    typename DOp<D>::T r;
+    r.x[0] = ld_shared<u32x4>(&t[at(row, col)]);
+    r.x[1] = ld_shared<u32x4>(&t[at(row, col + 8)]);
+    return r;
+  } else {
+    return ld_shared<typename DOp<D>::T>(&t[at(row, col)]);
+  }
+}
+
 // LD: how the bias tile reaches LDS.  16: 16-byte direct loads (N % 8 == 0); 4: 4-byte
 // direct loads, one per 256-byte bias row (N even); 0: through registers (N odd).
 // BP: dQ and dbias partials stored as bf16 (one RNE rounding each) instead of FP32.
@@ -91,7 +132,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr bool VEC = LD != 0;   // direct global->LDS path
   constexpr int NW = TK / 16;     // waves; wave w owns keys 16w..16w+15 of the tile
   constexpr int NT = NW * 64;
-  constexpr int TQ = kBwdQueryTile, G = bwd_group(D, VEC);
+  constexpr int TQ = bwd_query_tile(D), G = bwd_group(D, VEC);
   constexpr int NQB = TQ / 16;    // 16-query blocks of a stage
   constexpr int NST = TQ / 32;    // 32-query halves of a stage (dV / dK contraction steps)
   static_assert(TQ % 32 == 0, "query tile must be whole 32-query halves");
@@ -424,7 +465,10 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     write_rls(lset);
     __syncthreads();                   // also publishes the K and V tiles
-    if (lset == 0 && 2 < nst) load_stage_direct(2 / G, 2 % G, 2);
+    if (lset == 0 && 2 < nst) {
+      load_stage_direct(2 / G, 2 % G, 2);
+      if (2 % G == 0) load_bias_direct(2 / G, (2 / G) & 1);   // G = 2: stage 2 starts query tile 1
+    }
   } else {
     load_stage_regs(0, 0);
     load_bias_regs(0);
@@ -468,8 +512,11 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       if (gs > 0) dq_stage(j, gs - 1, dsb ^ 1, true);
       else dq_stage(j > 0 ? j - 1 : 0, G - 1, dsb ^ 1, j > 0);
 
-      const QT kb = ld_shared<QT>(&sK[gs][Lay<D>::k(16 * w + c, g * QL)]);
-      const QT vb = ld_shared<QT>(&sV[gs][Lay<D>::v(16 * w + c, g * QL)]);
+      const auto lk = [](int r, int cc) { return Lay<D>::k(r, cc); };
+      const auto lv = [](int r, int cc) { return Lay<D>::v(r, cc); };
+      const auto lq = [](int r, int cc) { return Lay<D>::q(r, cc); };
+      const QT kb = ld_op<D>(sK[gs], 16 * w + c, g * QL, lk);
+      const QT vb = ld_op<D>(sV[gs], 16 * w + c, g * QL, lv);
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
         u32x2 pP[2], pS[2];
@@ -478,8 +525,8 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
           const int qb = 2 * st + e;
           const int ql = 32 * st + 8 * (c >> 2) + 4 * e + (c & 3);
           const int r0 = 32 * st + 8 * g + 4 * e;
-          const QT qa = ld_shared<QT>(&tq[Lay<D>::q(ql, g * QL)]);
-          const QT da = ld_shared<QT>(&tdo[Lay<D>::q(ql, g * QL)]);
+          const QT qa = ld_op<D>(tq, ql, g * QL, lq);
+          const QT da = ld_op<D>(tdo, ql, g * QL, lq);
           const f32x4 nl = *reinterpret_cast<const f32x4*>(&sL[buf][r0]);
           const f32x4 nd = *reinterpret_cast<const f32x4*>(&sDl[buf][r0]);
           const f32x4 sv = DOp<D>::mma(qa, kb, nl);        // q.k - lse/scale
@@ -643,6 +690,12 @@ hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t s) {
   TRI_BWD_CASE(16, true, 4)
   TRI_BWD_CASE(16, false, 0)
   TRI_BWD_CASE(16, true, 0)
+  TRI_BWD_CASE(64, false, 16)
+  TRI_BWD_CASE(64, true, 16)
+  TRI_BWD_CASE(64, false, 4)
+  TRI_BWD_CASE(64, true, 4)
+  TRI_BWD_CASE(64, false, 0)
+  TRI_BWD_CASE(64, true, 0)
 #undef TRI_BWD_CASE
   return hipErrorInvalidValue;
 }

@@ -47,9 +47,20 @@ __device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
-// Contraction over the head dimension D (16 or 32) of one 16x16 block.
-// For D = 32 each lane supplies 8 values (slots d = 8g..8g+7), for D = 16 four (d = 4g..4g+3).
+// Contraction over the head dimension D (16, 32 or 64) of one 16x16 block.
+// For D = 32 each lane supplies 8 values (slots d = 8g..8g+7), for D = 16 four (d = 4g..4g+3),
+// for D = 64 sixteen (d = 16g..16g+15: two 16x16x32 products, d = 16g..16g+7 in the first).
 template <int D> struct DOp;
+struct u32x4x2 {
+  u32x4 x[2];
+};
+template <> struct DOp<64> {
+  typedef u32x4x2 T;
+  static constexpr int kPerLane = 16;
+  __device__ static __forceinline__ f32x4 mma(T a, T b, f32x4 c) {
+    return mfma_k32(a.x[1], b.x[1], mfma_k32(a.x[0], b.x[0], c));
+  }
+};
 template <> struct DOp<32> {
   typedef u32x4 T;
   static constexpr int kPerLane = 8;

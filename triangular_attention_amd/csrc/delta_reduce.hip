@@ -137,6 +137,7 @@ hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t s) {
   const bool res = a.o_res != nullptr;
   if (D == 32) return res ? launch_delta_t<32, true>(a, s) : launch_delta_t<32, false>(a, s);
   if (D == 16) return res ? launch_delta_t<16, true>(a, s) : launch_delta_t<16, false>(a, s);
+  if (D == 64) return res ? launch_delta_t<64, true>(a, s) : launch_delta_t<64, false>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -44,15 +44,28 @@
 
 namespace tri {
 
+// q * scale as a pair of bf16 terms per element, hi = bf16(x) and lo = bf16(x - hi).
+template <typename V>
+__device__ __forceinline__ void split_scaled(V q, float scale, V& hi, V& lo) {
+  constexpr int n = sizeof(V) / 4;
+#pragma unroll
+  for (int j = 0; j < n; ++j) {
+    const float x0 = bf_lo(q[j]) * scale, x1 = bf_hi(q[j]) * scale;
+    const uint32_t hw = pack_bf16(x0, x1);
+    hi[j] = hw;
+    lo[j] = pack_bf16(x0 - bf_lo(hw), x1 - bf_hi(hw));
+  }
+}
+
 // LD: width of the direct global->LDS loads of bias rows and mask values.  16: 16-byte
 // loads (N % 8 == 0); 4: 4-byte loads (N even); 0: bias and mask through registers (N odd).
 template <int D, bool MASK, int LD>
-__global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
   constexpr int TQ = kFwdQueryTile, TK = kFwdKeyTile;
   constexpr int KP = D;        // K / V tile pitch (bf16), one row per key, 16-byte chunks swizzled
   constexpr int CH = D / 8;    // 16-byte chunks of data per row
   constexpr int NKPIECE = TK * CH / 64;    // whole-wave 1 KB pieces per K (or V) tile
-  static_assert(NKPIECE == 2 || NKPIECE == 4, "K/V tiles must split over the four waves");
+  static_assert(NKPIECE == 2 || NKPIECE == 4 || NKPIECE == 8, "K/V tiles must split over the four waves");
   constexpr int NDB = D / 16;  // 16-wide feature blocks of O
   constexpr float kSumLimit = 0x1p64f;     // tile sum that forces a new reference maximum
   typedef typename DOp<D>::T QT;
@@ -106,15 +119,13 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
   for (int qb = 0; qb < 2; ++qb) {
     qrow[qb] = qt * TQ + 32 * w + 16 * qb + c;
     const uint32_t qo = (uint32_t)(qrow[qb] * D + g * QL) * 2;
-    QT q;
-    if constexpr (D == 32) q = buf_ld16(rQ, qo);
-    else q = buf_ld8(rQ, qo);
-#pragma unroll
-    for (int j = 0; j < QL / 2; ++j) {
-      const float x0 = bf_lo(q[j]) * a.scale, x1 = bf_hi(q[j]) * a.scale;
-      const uint32_t hw = pack_bf16(x0, x1);
-      qhi[qb][j] = hw;
-      qlo[qb][j] = pack_bf16(x0 - bf_lo(hw), x1 - bf_hi(hw));
+    if constexpr (D == 64) {
+      split_scaled(buf_ld16(rQ, qo), a.scale, qhi[qb].x[0], qlo[qb].x[0]);
+      split_scaled(buf_ld16(rQ, qo + 16), a.scale, qhi[qb].x[1], qlo[qb].x[1]);
+    } else if constexpr (D == 32) {
+      split_scaled(buf_ld16(rQ, qo), a.scale, qhi[qb], qlo[qb]);
+    } else {
+      split_scaled(buf_ld8(rQ, qo), a.scale, qhi[qb], qlo[qb]);
     }
     boff[qb] = (uint32_t)qrow[qb] * N * 2;
   }
@@ -138,7 +149,7 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
   // at position chunk ^ sw(r) (the source address of each lane is permuted, so the loads
   // stay whole-wave): the K operand reads and the transposing V^T reads then spread over
   // the LDS banks.  With D = 32 each wave loads one K and one V piece, with D = 16 one
-  // piece of K (waves 0, 1) or V (waves 2, 3).  With a mask, wave 0 also loads the tile's
+  // piece of K (waves 0, 1) or V (waves 2, 3), with D = 64 two pieces of each.  With a mask, wave 0 also loads the tile's
   // 64 mask values (lanes 0..15; the others read zeros past the end of the buffer).  With 16-byte aligned bias
   // rows (N % 8 == 0) each wave then loads its 32 bias rows of the tile (four pieces,
   // chunk position chunk ^ swb(row)); otherwise the bias goes through registers.
@@ -150,11 +161,16 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
   constexpr bool MLDS = MASK && LDSIN;
   auto sw = [](int r) { return (r >> 3) & (CH - 1); };
   auto swb = [](int r) { return (r >> 1) & 7; };   // bias rows: 8 chunks of 8 keys
-  uint32_t kv_off, m_off, b_off[4];
+  // kv_off[i]: the lane's source offset in the wave's i-th piece (pieces w and w + 4
+  // when D = 64)
+  uint32_t kv_off[2], m_off, b_off[4];
   {
-    const int piece = NKPIECE == 4 ? w : (w & 1);
-    const int row = piece * (64 / CH) + lane / CH, pos = lane % CH;
-    kv_off = (uint32_t)(row * D + (pos ^ sw(row)) * 8) * 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int piece = NKPIECE == 8 ? w + 4 * i : NKPIECE == 4 ? w : (w & 1);
+      const int row = piece * (64 / CH) + lane / CH, pos = lane % CH;
+      kv_off[i] = (uint32_t)(row * D + (pos ^ sw(row)) * 8) * 2;
+    }
     if (LD == 4) {
       // 4-byte loads: one load fills two 128-byte bias rows 2i, 2i+1 of the wave; lane l
       // takes row 2i + (l >> 5) and dword l & 31 of it, whose chunk position XOR swb =
@@ -186,8 +202,14 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
   };
   auto load_kv = [&](int kt, uint16_t* dK, uint16_t* dV, float* dM, uint16_t* dB) {
     const bool real = kt < nkt;
-    const uint32_t kvo = real ? (uint32_t)(kt * TK * D) * 2 + kv_off : kOOB;
-    if constexpr (NKPIECE == 4) {
+    const uint32_t kvo = real ? (uint32_t)(kt * TK * D) * 2 + kv_off[0] : kOOB;
+    if constexpr (NKPIECE == 8) {
+      const uint32_t kvo1 = real ? (uint32_t)(kt * TK * D) * 2 + kv_off[1] : kOOB;
+      ld2lds(rK, wK, dK + w * 512, kvo);
+      ld2lds(rK, wK, dK + (w + 4) * 512, kvo1);
+      ld2lds(rV, wV, dV + w * 512, kvo);
+      ld2lds(rV, wV, dV + (w + 4) * 512, kvo1);
+    } else if constexpr (NKPIECE == 4) {
       ld2lds(rK, wK, dK + w * 512, kvo);
       ld2lds(rV, wV, dV + w * 512, kvo);
     } else {
@@ -309,7 +331,12 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs a) {
       for (int e = 0; e < 2; ++e) {
         const int kl = 32 * m + 8 * (c >> 2) + 4 * e + (c & 3);
         const int kc = (g * QL) / 8;   // 16-byte chunk of this lane's features
-        ka[m][e] = ld_shared<QT>(&tK[kl * KP + ((kc ^ sw(kl)) * 8) + (g * QL) % 8]);
+        if constexpr (D == 64) {       // two chunks, each at its own swizzled position
+          ka[m][e].x[0] = ld_shared<u32x4>(&tK[kl * KP + ((kc ^ sw(kl)) * 8)]);
+          ka[m][e].x[1] = ld_shared<u32x4>(&tK[kl * KP + (((kc + 1) ^ sw(kl)) * 8)]);
+        } else {
+          ka[m][e] = ld_shared<QT>(&tK[kl * KP + ((kc ^ sw(kl)) * 8) + (g * QL) % 8]);
+        }
       }
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -487,6 +514,12 @@ hipError_t launch_fwd(const FwdArgs& a, int D, hipStream_t s) {
   TRI_FWD_CASE(16, true, 4)
   TRI_FWD_CASE(16, false, 0)
   TRI_FWD_CASE(16, true, 0)
+  TRI_FWD_CASE(64, false, 16)
+  TRI_FWD_CASE(64, true, 16)
+  TRI_FWD_CASE(64, false, 4)
+  TRI_FWD_CASE(64, true, 4)
+  TRI_FWD_CASE(64, false, 0)
+  TRI_FWD_CASE(64, true, 0)
 #undef TRI_FWD_CASE
   return hipErrorInvalidValue;
 }

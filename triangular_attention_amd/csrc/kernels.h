@@ -8,15 +8,18 @@ namespace tri {
 // Tile constants of the key-tile backward.  J_K = ceil(N / kBwdKeyTile) dQ
 // partials and L = ceil(N_o / G) dbias partials, G = bwd_group(D, N % 8 == 0)
 // outer slices per workgroup: dK and dV of G slices stay in registers, so G is
-// 4 for D = 32 and 6 for D = 16 (half the accumulator registers per slice; 8
-// spills; the register-staged path for odd N has no room and keeps 4).
+// 4 for D = 32, 6 for D = 16 (half the accumulator registers per slice; 8
+// spills; the register-staged path for odd N has no room and keeps 4) and 2 for
+// D = 64 (twice the registers per slice).
 constexpr int kBwdKeyTile = 128;
-constexpr int bwd_group(int D, bool vec) { return (D == 16 && vec) ? 6 : 4; }
+constexpr int bwd_group(int D, bool vec) { return D == 64 ? 2 : (D == 16 && vec) ? 6 : 4; }
 // Width of the direct global->LDS loads of bias rows (N bf16 per row): 16 bytes when
 // rows are 16-byte aligned, 4 bytes when they are 4-byte aligned, 0 = no direct loads
 // (odd N: rows go through registers).  `vec` above means a nonzero width.
 constexpr int bias_load_width(int N) { return N % 8 == 0 ? 16 : (N % 2 == 0 ? 4 : 0); }
-constexpr int kBwdQueryTile = 64;
+// Queries per backward stage: 64, or 32 for D = 64 (its Q / dO stage buffers and
+// dQ blocks per stage then match those of D = 32).
+constexpr int bwd_query_tile(int D) { return D == 64 ? 32 : 64; }
 constexpr int kFwdQueryTile = 128;
 constexpr int kFwdKeyTile = 64;
 
