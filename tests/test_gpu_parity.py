@@ -191,9 +191,9 @@ def test_python_validation_on_device():
         ta.forward(q, q, q, bias[:, :, :4])
     with pytest.raises(ValueError):
         ta.forward(q.transpose(3, 4).contiguous().transpose(3, 4), q, q, bias)
-    q64 = torch.zeros(1, 2, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
+    q48 = torch.zeros(1, 2, 1, 8, 48, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ta.TriAttnError):
-        ta.forward(q64, q64, q64, bias)
+        ta.forward(q48, q48, q48, bias)
 
 
 @pytest.mark.parametrize("case", [(9, 72, 3, 32, 0.1, 1.0, 1), (5, 100, 2, 32, 0.3, 2.0, 2), (8, 96, 2, 16, 0.15, 1.0, 1),
