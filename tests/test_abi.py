@@ -261,7 +261,7 @@ def test_trimul_workspace_counts(lib, B, N, c):
     assert lib.tri_mul_workspace(ctypes.byref(d), *[ctypes.byref(v) for v in vals]) == 0
     pairs = B * N * N
     splits = (4 * c + 128) // 128
-    assert vals[0].value == min(-(-pairs // 64), 8 * (256 // (8 * splits)))
+    assert vals[0].value == min(-(-pairs // 64), 8 * (512 // (8 * splits)))
     assert vals[1].value == min(-(-pairs // 64), 256)
     assert vals[2].value == min(-(-pairs // 32), 256)
     assert vals[3].value == vals[1].value * (128 // c)

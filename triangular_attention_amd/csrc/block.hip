@@ -622,25 +622,43 @@ __global__ __launch_bounds__(NT) void proj_dw_kernel(BlkProjBwdArgs a) {
   }
 }
 
-// Fixed-order sum of partial buffers: out[e] = sum_{i = 0..n-1} partial[i][e], ascending i.
-// Loads are issued 16 partials at a time (independent), the adds stay in ascending order.
+// Fixed-order sum of partial buffers, out[e] = sum over i of partial[i][e], for elems % 4 == 0.
+// Lane l of a wave owns elements 4 (l mod 16) .. +3 of the wave's 64-element chunk and the
+// partials i = l / 16 (mod 4), added in ascending i; the four lane sums are then combined as
+// (s0 + s1) + (s2 + s3).  The tree depends only on n, so every call gives the same bits.
+// Loads are 16 bytes, 8 partials in flight per lane.
 __global__ __launch_bounds__(256) void blk_reduce_kernel(BlkReduceArgs a) {
-  constexpr int U = 16;
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= a.elems) return;
-  const float* p = a.partial + e;
-  float s = 0.f;
-  int i = 0;
-  for (; i + U <= a.n; i += U) {
-    float v[U];
+  constexpr int U = 8;
+  const int lane = threadIdx.x & 63, j = lane >> 4;
+  const int64_t e0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64 + 4 * (lane & 15);
+  if (e0 >= a.elems) return;   // the four lanes of a chunk leave together
+  const float* p = a.partial + e0;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  int i = j;
+  for (; i + 4 * (U - 1) < a.n; i += 4 * U) {
+    f32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + (size_t)(i + u) * a.elems);
+    for (int u = 0; u < U; ++u)
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + (size_t)(i + 4 * u) * a.elems));
 #pragma unroll
     for (int u = 0; u < U; ++u) s += v[u];
   }
-  for (; i < a.n; ++i) s += p[(size_t)i * a.elems];
-  if (e < a.split) a.out0[e] = s;
-  else a.out1[e - a.split] = s;
+  for (; i < a.n; i += 4) s += *reinterpret_cast<const f32x4*>(p + (size_t)i * a.elems);
+#pragma unroll
+  for (int m = 16; m <= 32; m <<= 1) {
+    f32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = __shfl_xor(s[k], m);
+    s = s + o;
+  }
+  if (j == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t e = e0 + k;
+      if (e < a.split) a.out0[e] = s[k];
+      else a.out1[e - a.split] = s[k];
+    }
+  }
 }
 
 }  // namespace
@@ -674,7 +692,8 @@ hipError_t launch_blk_proj_dw(const BlkProjBwdArgs& a, hipStream_t st) {
 
 hipError_t launch_blk_reduce(const BlkReduceArgs& a, hipStream_t st) {
   if (a.elems == 0) return hipSuccess;
-  const int64_t blocks = (a.elems + 255) / 256;
+  if (a.elems % 4 != 0) return hipErrorInvalidValue;   // every weight shape here is a multiple of 4
+  const int64_t blocks = (a.elems + 255) / 256;   // one lane per element (4 lanes per 4 elements)
   hipLaunchKernelGGL(blk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }

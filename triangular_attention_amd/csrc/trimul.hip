@@ -826,7 +826,7 @@ __global__ __launch_bounds__(NT) void tm_in_dw_kernel(TmInGradArgs a) {
   const int N = a.s.N, inc = a.s.incoming;
   const int total = a.s.B * N * N;
   const int ntiles = (total + TP - 1) / TP;
-  const int cap = 8 * (kTmMaxWG / (8 * NSPLIT));
+  const int cap = 8 * (kTmDwMaxWG / (8 * NSPLIT));
   const int groups = ntiles < cap ? ntiles : cap;
   const int bx = blockIdx.x, kx = bx >> 3;
   const int split = kx % NSPLIT, grp = (kx / NSPLIT) * 8 + (bx & 7);

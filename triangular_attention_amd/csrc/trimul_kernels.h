@@ -16,6 +16,7 @@ constexpr int kTmTileOutBwd = 64;  // pairs per tile: output step, backward
 constexpr int kTmTileDz = 32;      // pairs per tile: dZ of the input projections
 constexpr int kTmTileDw = 64;      // pairs per tile: weight gradient of the input projections
 constexpr int kTmMaxWG = 256;
+constexpr int kTmDwMaxWG = 512;    // the input weight-gradient kernel fits two workgroups per CU
 
 inline int64_t tm_grid(int64_t pairs, int tile) {
   const int64_t t = (pairs + tile - 1) / tile;
@@ -26,7 +27,7 @@ inline int64_t tm_grid(int64_t pairs, int tile) {
 inline int tm_dw_splits(int c) { return (4 * c + kTmC) / 128; }
 inline int64_t tm_dw_groups(int64_t pairs, int c) {
   const int64_t t = (pairs + kTmTileDw - 1) / kTmTileDw;
-  const int64_t cap = 8 * (kTmMaxWG / (8 * tm_dw_splits(c)));
+  const int64_t cap = 8 * (kTmDwMaxWG / (8 * tm_dw_splits(c)));
   return t < cap ? t : cap;
 }
 
