@@ -663,10 +663,10 @@ __global__ __launch_bounds__(256) void blk_reduce_kernel(BlkReduceArgs a) {
 
 }  // namespace
 
-#define TRI_BLK_LAUNCH(KERNEL, ARGS, TILE)                                                   \
+#define TRI_BLK_LAUNCH(KERNEL, ARGS, TILE, CAP)                                              \
   {                                                                                            \
     const int64_t pairs = (int64_t)(ARGS).s.B * (ARGS).s.N * (ARGS).s.N;                       \
-    const int grid = (int)blk_grid(pairs, TILE);                                               \
+    const int grid = (int)blk_grid(pairs, TILE, CAP);                                          \
     if (grid == 0) return hipSuccess;                                                          \
     if ((ARGS).s.D == 32)                                                                      \
       hipLaunchKernelGGL((KERNEL<4, 32>), dim3(grid), dim3(NT), 0, st, ARGS);                  \
@@ -675,11 +675,14 @@ __global__ __launch_bounds__(256) void blk_reduce_kernel(BlkReduceArgs a) {
     return hipGetLastError();                                                                  \
   }
 
-hipError_t launch_blk_ln_proj(const BlkLnProjArgs& a, hipStream_t st) TRI_BLK_LAUNCH(ln_proj_kernel, a, kBlkTileFwd)
-hipError_t launch_blk_gate_out(const BlkGateOutArgs& a, hipStream_t st) TRI_BLK_LAUNCH(gate_out_kernel, a, kBlkTileFwd)
+hipError_t launch_blk_ln_proj(const BlkLnProjArgs& a, hipStream_t st)
+    TRI_BLK_LAUNCH(ln_proj_kernel, a, kBlkTileFwd, kBlkMaxWG)
+hipError_t launch_blk_gate_out(const BlkGateOutArgs& a, hipStream_t st)
+    TRI_BLK_LAUNCH(gate_out_kernel, a, kBlkTileFwd, kBlkMaxWG)
 hipError_t launch_blk_gate_out_bwd(const BlkGateOutArgs& a, hipStream_t st)
-    TRI_BLK_LAUNCH(gate_out_bwd_kernel, a, kBlkTileOutBwd)
-hipError_t launch_blk_proj_dz(const BlkProjBwdArgs& a, hipStream_t st) TRI_BLK_LAUNCH(proj_dz_kernel, a, kBlkTileProjBwd)
+    TRI_BLK_LAUNCH(gate_out_bwd_kernel, a, kBlkTileOutBwd, kBlkMaxWG)
+hipError_t launch_blk_proj_dz(const BlkProjBwdArgs& a, hipStream_t st)
+    TRI_BLK_LAUNCH(proj_dz_kernel, a, kBlkTileProjBwd, kBlkMaxWG)
 hipError_t launch_blk_proj_dw(const BlkProjBwdArgs& a, hipStream_t st) {
   const int64_t pairs = (int64_t)a.s.B * a.s.N * a.s.N;
   const int64_t groups = blk_dw_groups(pairs);

@@ -18,9 +18,9 @@ constexpr int kBlkTileOutBwd = 128; // pairs per tile: backward of gate + output
 constexpr int kBlkTileProjBwd = 64; // pairs per tile: backward of the projections
 
 // Workgroups (= partial buffers) of a persistent launch over `pairs` pairs in tiles of `tile`.
-inline int64_t blk_grid(int64_t pairs, int tile) {
+inline int64_t blk_grid(int64_t pairs, int tile, int cap = kBlkMaxWG) {
   const int64_t t = (pairs + tile - 1) / tile;
-  return t < kBlkMaxWG ? t : kBlkMaxWG;
+  return t < cap ? t : cap;
 }
 
 // Tile groups (= partial buffers) of the weight-gradient kernel: two workgroups per group.

@@ -385,8 +385,9 @@ __global__ __launch_bounds__(256) void tm_gemm_kernel(TmGemmArgs p) {
 
 // ----------------------------------------------------------------------------------------------
 // Output step.  Tile = 128 update pairs; the contraction tile is staged [channel][pair].
+// c = 64: two workgroups per CU (at most 128 VGPRs); c = 128 keeps one (it would spill)
 template <int CH>
-__global__ __launch_bounds__(NT) void tm_out_fwd_kernel(TmOutArgs a) {
+__global__ __launch_bounds__(NT, CH == 64 ? 4 : 2) void tm_out_fwd_kernel(TmOutArgs a) {
   constexpr int TP = kTmTileOut;
   constexpr int NQ = CH / 4;                 // channels per thread in the statistics passes
   constexpr int NLD = CH * TP / 8 / NT;      // 16-byte chunks per thread of a contraction tile
@@ -890,9 +891,9 @@ __global__ __launch_bounds__(NT) void tm_in_dw_kernel(TmInGradArgs a) {
 }
 
 template <typename Args, typename K64, typename K128>
-hipError_t launch_pairs(const Args& a, int tile, K64 k64, K128 k128, hipStream_t st) {
+hipError_t launch_pairs(const Args& a, int tile, K64 k64, K128 k128, hipStream_t st, int cap = kTmMaxWG) {
   const int64_t pairs = (int64_t)a.s.B * a.s.N * a.s.N;
-  const int grid = (int)tm_grid(pairs, tile);
+  const int grid = (int)tm_grid(pairs, tile, cap);
   if (grid == 0) return hipSuccess;
   if (a.s.c == 128) hipLaunchKernelGGL(k128, dim3(grid), dim3(NT), 0, st, a);
   else hipLaunchKernelGGL(k64, dim3(grid), dim3(NT), 0, st, a);
@@ -917,7 +918,8 @@ hipError_t launch_tm_in_bwd(const TmInArgs& a, hipStream_t st) {
   return launch_pairs(a, kTmTileIn, tm_in_bwd_kernel<64>, tm_in_bwd_kernel<128>, st);
 }
 hipError_t launch_tm_out_fwd(const TmOutArgs& a, hipStream_t st) {
-  return launch_pairs(a, kTmTileOut, tm_out_fwd_kernel<64>, tm_out_fwd_kernel<128>, st);
+  return launch_pairs(a, kTmTileOut, tm_out_fwd_kernel<64>, tm_out_fwd_kernel<128>, st,
+                      a.s.c == 64 ? kTmOutMaxWG : kTmMaxWG);
 }
 hipError_t launch_tm_out_bwd(const TmOutArgs& a, hipStream_t st) {
   return launch_pairs(a, kTmTileOutBwd, tm_out_bwd_kernel<64>, tm_out_bwd_kernel<128>, st);

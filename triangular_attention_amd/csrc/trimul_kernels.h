@@ -17,10 +17,11 @@ constexpr int kTmTileDz = 32;      // pairs per tile: dZ of the input projection
 constexpr int kTmTileDw = 64;      // pairs per tile: weight gradient of the input projections
 constexpr int kTmMaxWG = 256;
 constexpr int kTmDwMaxWG = 512;    // the input weight-gradient kernel fits two workgroups per CU
+constexpr int kTmOutMaxWG = 512;   // so does the output step's forward with c = 64 (no partials)
 
-inline int64_t tm_grid(int64_t pairs, int tile) {
+inline int64_t tm_grid(int64_t pairs, int tile, int cap = kTmMaxWG) {
   const int64_t t = (pairs + tile - 1) / tile;
-  return t < kTmMaxWG ? t : kTmMaxWG;
+  return t < cap ? t : cap;
 }
 // Workgroups per tile group of the input weight gradient (128 rows of d w_in each) and the
 // number of tile groups (= partial buffers).
