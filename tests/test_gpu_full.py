@@ -108,6 +108,25 @@ def test_bitwise_replay(shape):
                                    first[n].view(torch.int32)), (n, seed)
 
 
+def test_bitwise_replay_d64():
+    """The D = 64 kernels (outer group 2) under the same protocol: five NaN-poisoned calls per
+    input, two seeded inputs (one masked), every output bitwise identical."""
+    ta = require_gpu()
+    w = synth.get("n768_d64_mask")
+    for seed in (1000, 1001):
+        print(f"replay n768 d64 seed {seed}", flush=True)
+        ww = w if seed % 2 else w.with_(mask_p=0.0)
+        dev = synth.make_inputs_device(ww, seed)
+        first = _poisoned_call(ta, dev, w.scale)
+        for n in ("dq", "dk", "dv", "dbias", "o"):
+            assert torch.isfinite(first[n].float()).all(), (n, seed)
+        for _ in range(4):
+            again = _poisoned_call(ta, dev, w.scale)
+            for n in ("dq", "dk", "dv", "dbias", "o", "lse"):
+                bits = torch.int16 if first[n].dtype == torch.bfloat16 else torch.int32
+                assert torch.equal(again[n].view(bits), first[n].view(bits)), (n, seed)
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_residual_compensation_ablation(name):
     ta = require_gpu()

@@ -538,6 +538,8 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
   const auto sr = make_rsrc(a.stats_o, (uint32_t)total * 8);
   u32x4 xv[NLD];
   f32x2 stv;                // statistics of this thread's pair pp
+  // this lane's incoming gradient and gate logits (4 features of one pair per block)
+  u32x2 dln[TP / 16], gln[TP / 16];
   auto load = [&](int tile) {
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
@@ -547,7 +549,15 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
     }
     const int rp = tile * TP + pp;
     stv = __builtin_bit_cast(f32x2, buf_ld8(sr, rp < total ? (uint32_t)rp * 8 : (uint32_t)total * 8));
+#pragma unroll
+    for (int pb = 0; pb < TP / 16; ++pb) {
+      const int r = tile * TP + 16 * pb + c;
+      const uint32_t o = r < total ? (uint32_t)(r * C + 16 * w + 4 * g) * 2 : pbytes;
+      dln[pb] = buf_ld8(dr, o);
+      gln[pb] = buf_ld8(gr, o);
+    }
   };
+  // everything a tile reads from memory is requested one tile ahead
   if ((int)blockIdx.x < ntiles) load(blockIdx.x);
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     lds_barrier();
@@ -557,18 +567,11 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
       st_lds16(sX, coff(q / SEGS, 8 * (q % SEGS)), xv[k]);
     }
     const f32x2 s = stv;
-    const int nt = tile + gridDim.x;
-    if (nt < ntiles) load(nt);
-    // this lane's incoming gradient and gate logits (4 features of one pair per block), in
-    // flight while the tile is normalised
     u32x2 dlv[TP / 16], glv[TP / 16];
 #pragma unroll
-    for (int pb = 0; pb < TP / 16; ++pb) {
-      const int r = tile * TP + 16 * pb + c;
-      const uint32_t o = r < total ? (uint32_t)(r * C + 16 * w + 4 * g) * 2 : pbytes;
-      dlv[pb] = buf_ld8(dr, o);
-      glv[pb] = buf_ld8(gr, o);
-    }
+    for (int pb = 0; pb < TP / 16; ++pb) { dlv[pb] = dln[pb]; glv[pb] = gln[pb]; }
+    const int nt = tile + gridDim.x;
+    if (nt < ntiles) load(nt);
     {
       if (qq == 0) { sSt[pp][0] = s[0]; sSt[pp][1] = s[1]; }
       lds_barrier();
