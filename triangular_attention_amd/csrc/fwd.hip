@@ -159,7 +159,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
   constexpr uint32_t kOOB = 0xFFFFF000u;       // any offset past every buffer
   constexpr bool LDSIN = LD != 0;              // mask and bias through LDS (aligned rows)
   constexpr bool MLDS = MASK && LDSIN;
-  auto sw = [](int r) { return (r >> 3) & (CH - 1); };
+  // chunk XOR of K / V row r.  D = 64: per half-wave the K reads touch four rows of equal
+  // (r mod 4) that differ in bits 3-4, two chunks each, and the transposing V^T reads four
+  // rows of equal parity that differ in bits 1 and 3; the XOR values below put every such
+  // set on distinct positions.
+  auto sw = [](int r) {
+    if constexpr (D == 64) return (((r >> 1) & 1) * 2) ^ (((r >> 3) & 1) * 5) ^ (((r >> 4) & 1) * 4);
+    else return (r >> 3) & (CH - 1);
+  };
   auto swb = [](int r) { return (r >> 1) & 7; };   // bias rows: 8 chunks of 8 keys
   // kv_off[i]: the lane's source offset in the wave's i-th piece (pieces w and w + 4
   // when D = 64)
