@@ -1,7 +1,7 @@
 // Shared device helpers for the gfx950 triangular-attention kernels.
 //
-// MFMA operand convention used by every kernel (v_mfma_f32_16x16x32_bf16 and
-// v_mfma_f32_16x16x16_bf16): lane l = 16*g + c (g = lane group 0..3, c = 0..15).
+// MFMA operand convention used by every kernel (v_mfma_f32_16x16x32_bf16):
+// lane l = 16*g + c (g = lane group 0..3, c = 0..15).
 //   A operand: lane (g, c) supplies row c of A and the contraction slots of group g.
 //   B operand: lane (g, c) supplies column c of B and the slots of group g.
 //   Result:    lane (g, c) holds rows 4g+0..3 of column c.
@@ -42,10 +42,6 @@ __device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
 
 // Contraction over the head dimension D (16, 32 or 64) of one 16x16 block.
 // For D = 32 each lane supplies 8 values (slots d = 8g..8g+7), for D = 16 four (d = 4g..4g+3),
@@ -66,10 +62,15 @@ template <> struct DOp<32> {
   static constexpr int kPerLane = 8;
   __device__ static __forceinline__ f32x4 mma(T a, T b, f32x4 c) { return mfma_k32(a, b, c); }
 };
+// D = 16 runs as a 16x16x32 product with slots 8g+4..8g+7 zero: on gfx950 it takes as long as
+// the 16x16x16 form, and the compiler's wait states after a 16x16x16 product are too short
+// for a dependent read of its result.
 template <> struct DOp<16> {
   typedef u32x2 T;
   static constexpr int kPerLane = 4;
-  __device__ static __forceinline__ f32x4 mma(T a, T b, f32x4 c) { return mfma_k16(a, b, c); }
+  __device__ static __forceinline__ f32x4 mma(T a, T b, f32x4 c) {
+    return mfma_k32(u32x4{a[0], a[1], 0u, 0u}, u32x4{b[0], b[1], 0u, 0u}, c);
+  }
 };
 
 // Raw buffer access: 32-bit byte offsets from a uniform base; reads past

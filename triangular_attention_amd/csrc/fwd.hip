@@ -130,25 +130,30 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
     boff[qb] = (uint32_t)qrow[qb] * N * 2;
   }
 
-  // identity block (A operand of the 16x16x16 product): lane (g, c) holds
-  // row c, slots 4g..4g+3
-  u32x2 ident;
+  // identity blocks (A operands of 16x16x32 products, one per half e of the 8 bias keys
+  // a lane group holds): lane (g, c) holds row c, slots 8g..8g+7, and row c picks slot
+  // 4e + (c mod 4) of group c / 4.  (A 16x16x16 product would need half the registers, but
+  // gfx950 runs it as long as the 16x16x32 one and the compiler's wait states after it are
+  // too short for a dependent read, so this file uses 16x16x32 products only.)
+  u32x4 ident[2];
   {
     const int i = c & 3;
     const bool mine = (c >> 2) == g;
     const uint32_t one = (i & 1) ? 0x3F800000u : 0x3F80u;
-    ident[0] = (mine && i < 2) ? one : 0u;
-    ident[1] = (mine && i >= 2) ? one : 0u;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) ident[e][wd] = (mine && wd == 2 * e + (i >> 1)) ? one : 0u;
   }
 
   const int nkt = (N + TK - 1) / TK;
   const bool ragged = (N % TK) != 0;
 
   // Direct global->LDS loads of a tile, in whole-wave pieces (lane l of a piece fills
-  // 16-byte slot l).  K and V tiles are unpadded, with the 16-byte chunks of row r stored
-  // at position chunk ^ sw(r) (the source address of each lane is permuted, so the loads
-  // stay whole-wave): the K operand reads and the transposing V^T reads then spread over
-  // the LDS banks.  With D = 32 each wave loads one K and one V piece, with D = 16 one
+  // 16-byte slot l).  K and V tiles are unpadded, with row r stored at row position pr(r)
+  // and its 16-byte chunks at positions chunk ^ sw(r) (the source address of each lane is
+  // permuted, so the loads stay whole-wave): the K operand reads and the transposing V^T
+  // reads then spread over the LDS banks.  With D = 32 each wave loads one K and one V piece, with D = 16 one
   // piece of K (waves 0, 1) or V (waves 2, 3), with D = 64 two pieces of each.  With a mask, wave 0 also loads the tile's
   // 64 mask values (lanes 0..15; the others read zeros past the end of the buffer).  With 16-byte aligned bias
   // rows (N % 8 == 0) each wave then loads its 32 bias rows of the tile (four pieces,
@@ -159,14 +164,23 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
   constexpr uint32_t kOOB = 0xFFFFF000u;       // any offset past every buffer
   constexpr bool LDSIN = LD != 0;              // mask and bias through LDS (aligned rows)
   constexpr bool MLDS = MASK && LDSIN;
-  // chunk XOR of K / V row r.  D = 64: per half-wave the K reads touch four rows of equal
-  // (r mod 4) that differ in bits 3-4, two chunks each, and the transposing V^T reads four
-  // rows of equal parity that differ in bits 1 and 3; the XOR values below put every such
-  // set on distinct positions.
+  // K / V tile layout: row position pr(r) and chunk XOR sw(r).  Per half-wave the K reads
+  // touch 16 rows (bits 0-1 and 3-4 varying) at two chunks each and the transposing V^T reads
+  // 8 rows (bits 0-1 and 3) at two chunks each.  D = 32 (64-byte rows, 8 rows per 512 bytes):
+  // bit 2 of the position flips with bit 4 and the chunk XOR is 2 with bit 3, which puts both
+  // on distinct 16-byte slots / 8-byte units.  D = 64 (128-byte rows): the chunk XOR alone
+  // (bit 1 -> 2, bit 3 -> 5, bit 4 -> 4) does it.  An involution: pr(pr(r)) = r.
+  auto pr = [](int r) {
+    if constexpr (D == 32) return r ^ (((r >> 4) & 1) << 2);
+    else return r;
+  };
   auto sw = [](int r) {
     if constexpr (D == 64) return (((r >> 1) & 1) * 2) ^ (((r >> 3) & 1) * 5) ^ (((r >> 4) & 1) * 4);
+    else if constexpr (D == 32) return ((r >> 3) & 1) * 2;
     else return (r >> 3) & (CH - 1);
   };
+  // element offset of (row r, column col) in a K or V tile
+  auto kv_at = [&](int r, int col) { return pr(r) * KP + (((col >> 3) ^ sw(r)) * 8) + (col & 7); };
   auto swb = [](int r) { return (r >> 1) & 7; };   // bias rows: 8 chunks of 8 keys
   // kv_off[i]: the lane's source offset in the wave's i-th piece (pieces w and w + 4
   // when D = 64)
@@ -175,7 +189,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int piece = NKPIECE == 8 ? w + 4 * i : NKPIECE == 4 ? w : (w & 1);
-      const int row = piece * (64 / CH) + lane / CH, pos = lane % CH;
+      // slot (position row, position chunk) holds logical row pr(position row)
+      const int row = pr(piece * (64 / CH) + lane / CH), pos = lane % CH;
       kv_off[i] = (uint32_t)(row * D + (pos ^ sw(row)) * 8) * 2;
     }
     if (LD == 4) {
@@ -325,8 +340,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-          sacc[qb][m][e] = mfma_k16(ident, u32x2{rb[qb][m][2 * e], rb[qb][m][2 * e + 1]},
-                                    MASK ? rm[m][e] : f32x4{0.f, 0.f, 0.f, 0.f});
+          sacc[qb][m][e] = mfma_k32(ident[e], rb[qb][m], MASK ? rm[m][e] : f32x4{0.f, 0.f, 0.f, 0.f});
     if constexpr (!LDSIN) {
       if (kt + 1 < nkt) load_bm(kt + 1);
     }
@@ -339,24 +353,38 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
         const int kl = 32 * m + 8 * (c >> 2) + 4 * e + (c & 3);
         const int kc = (g * QL) / 8;   // 16-byte chunk of this lane's features
         if constexpr (D == 64) {       // two chunks, each at its own swizzled position
-          ka[m][e].x[0] = ld_shared<u32x4>(&tK[kl * KP + ((kc ^ sw(kl)) * 8)]);
-          ka[m][e].x[1] = ld_shared<u32x4>(&tK[kl * KP + (((kc + 1) ^ sw(kl)) * 8)]);
+          ka[m][e].x[0] = ld_shared<u32x4>(&tK[kv_at(kl, 8 * kc)]);
+          ka[m][e].x[1] = ld_shared<u32x4>(&tK[kv_at(kl, 8 * kc + 8)]);
         } else {
-          ka[m][e] = ld_shared<QT>(&tK[kl * KP + ((kc ^ sw(kl)) * 8) + (g * QL) % 8]);
+          ka[m][e] = ld_shared<QT>(&tK[kv_at(kl, g * QL)]);
         }
       }
+    if constexpr (D == 16) {
+      // one 16x16x32 product per block takes both terms: slots 8g..8g+3 hold the K
+      // features against the hi terms, 8g+4..8g+7 the same features against the lo terms
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
+        for (int e = 0; e < 2; ++e) {
+          const u32x4 kk = u32x4{ka[m][e][0], ka[m][e][1], ka[m][e][0], ka[m][e][1]};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) sacc[qb][m][e] = DOp<D>::mma(ka[m][e], qlo[qb], sacc[qb][m][e]);
+          for (int qb = 0; qb < 2; ++qb)
+            sacc[qb][m][e] = mfma_k32(kk, u32x4{qhi[qb][0], qhi[qb][1], qlo[qb][0], qlo[qb][1]}, sacc[qb][m][e]);
+        }
+    } else {
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
+        for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) sacc[qb][m][e] = DOp<D>::mma(ka[m][e], qhi[qb], sacc[qb][m][e]);
+          for (int qb = 0; qb < 2; ++qb) sacc[qb][m][e] = DOp<D>::mma(ka[m][e], qlo[qb], sacc[qb][m][e]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) sacc[qb][m][e] = DOp<D>::mma(ka[m][e], qhi[qb], sacc[qb][m][e]);
+    }
 
     if (TAIL) {
 #pragma unroll
@@ -381,8 +409,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
         // lane (k, a) of its group: rows r0 + k and r0 + 4 + k, columns 16 db + 4a .. +3
         const int k = (lane & 15) >> 2, a4 = 16 * db + 4 * (lane & 3);
         const int r0 = 32 * m + 8 * g + k, r1 = r0 + 4;
-        va[m][db] = ds_read_tr8_at(tV, r0 * KP + (((a4 >> 3) ^ sw(r0)) * 8) + (a4 & 7),
-                                   r1 * KP + (((a4 >> 3) ^ sw(r1)) * 8) + (a4 & 7));
+        va[m][db] = ds_read_tr8_at(tV, kv_at(r0, a4), kv_at(r1, a4));
       }
 
 #pragma unroll
