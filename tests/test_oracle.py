@@ -117,9 +117,9 @@ def _close(a, b, tol):
     return np.max(np.abs(a - b)) <= tol * max(1.0, float(np.max(np.abs(b))))
 
 
-@pytest.mark.parametrize("mask_p", [0.0, 0.3])
-def test_grads_match_torch_autograd(mask_p):
-    w, x = _inputs(4, 6, 2, 4, seed=5, mask_p=mask_p)
+@pytest.mark.parametrize("mask_p,D", [(0.0, 4), (0.3, 4), (0.2, 64)])
+def test_grads_match_torch_autograd(mask_p, D):
+    w, x = _inputs(4, 6, 2, D, seed=5, mask_p=mask_p)
     g = oracle.backward(x["q"], x["k"], x["v"], x["bias"], x["mask"], w.scale, x["do"])
     tg, O = _torch_grads(x, x["mask"], w.scale)
     assert _close(g["o"], O, 1e-12)
