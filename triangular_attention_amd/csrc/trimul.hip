@@ -25,6 +25,8 @@
 //                on one XCD so that the shared Z tiles come from its L2)
 // All products are bf16 MFMA (v_mfma_f32_16x16x32_bf16) with FP32 accumulation; no MFMA
 // sits in a lane-masked branch (the matrix cores ignore EXEC).
+#include <type_traits>
+
 #include "common.h"
 #include "pair_common.h"
 #include "trimul_kernels.h"
@@ -732,37 +734,44 @@ __global__ __launch_bounds__(NT) void tm_in_dz_kernel(TmInGradArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { gm[i] = a.gamma[c0 + i]; dgam[i] = 0.f; dbet[i] = 0.f; }
 
-  // loader: one chunk per segment per thread (pair t >> 4, chunk t & 15)
+  // loader: one chunk per segment per thread (pair t >> 4, chunk t & 15).  Two register
+  // sets: the loads of a tile are issued two tiles ahead (set K serves every other tile).
   const int lp = t >> 4, lj = t & 15;
-  u32x4 pv[NS];
-  u32x2 zq[TP / 16];
-  f32x2 st[TP / 16];
-  auto load = [&](int tile) {
+  u32x4 pv[2][NS];
+  u32x2 zq[2][TP / 16];
+  f32x2 st[2][TP / 16];
+  auto load = [&](int tile, auto k_c) {
+    constexpr int K = decltype(k_c)::value;
     const int r = tile * TP + lp;
     const bool ok = r < total;
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
-      pv[s] = buf_ld16(pr, ok ? (uint32_t)((size_t)r * 4 * CH + 128 * s + 8 * lj) * 2 : pbytes);
-    pv[NS - 1] = buf_ld16(gr, ok ? (uint32_t)(zrow(pair_ix(r, N), N, inc) + 8 * lj) * 2 : zbytes);
+      pv[K][s] = buf_ld16(pr, ok ? (uint32_t)((size_t)r * 4 * CH + 128 * s + 8 * lj) * 2 : pbytes);
+    pv[K][NS - 1] = buf_ld16(gr, ok ? (uint32_t)(zrow(pair_ix(r, N), N, inc) + 8 * lj) * 2 : zbytes);
 #pragma unroll
     for (int pb = 0; pb < TP / 16; ++pb) {
       const int rr = tile * TP + 16 * pb + c;
       const bool ok2 = rr < total;
-      zq[pb] = buf_ld8(zr, ok2 ? (uint32_t)(zrow(pair_ix(rr, N), N, inc) + c0) * 2 : zbytes);
-      st[pb] = __builtin_bit_cast(f32x2, buf_ld8(sr, ok2 ? (uint32_t)rr * 8 : (uint32_t)total * 8));
+      zq[K][pb] = buf_ld8(zr, ok2 ? (uint32_t)(zrow(pair_ix(rr, N), N, inc) + c0) * 2 : zbytes);
+      st[K][pb] = __builtin_bit_cast(f32x2, buf_ld8(sr, ok2 ? (uint32_t)rr * 8 : (uint32_t)total * 8));
     }
   };
-  if ((int)blockIdx.x < ntiles) load(blockIdx.x);
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  const int gs = gridDim.x;
+  if ((int)blockIdx.x < ntiles) load(blockIdx.x, S0{});
+  if ((int)blockIdx.x + gs < ntiles) load(blockIdx.x + gs, S1{});
+  auto body = [&](int tile, auto k_c) {
+    constexpr int K = decltype(k_c)::value;
     lds_barrier();
 #pragma unroll
-    for (int s = 0; s < NS; ++s) st_lds16(sP[s], toff(lp, lj), pv[s]);
+    for (int s = 0; s < NS; ++s) st_lds16(sP[s], toff(lp, lj), pv[K][s]);
     u32x2 zc[TP / 16];
     f32x2 sc[TP / 16];
 #pragma unroll
-    for (int pb = 0; pb < TP / 16; ++pb) { zc[pb] = zq[pb]; sc[pb] = st[pb]; }
-    const int nt = tile + gridDim.x;
-    if (nt < ntiles) load(nt);
+    for (int pb = 0; pb < TP / 16; ++pb) { zc[pb] = zq[K][pb]; sc[pb] = st[K][pb]; }
+    const int nt = tile + 2 * gs;
+    if (nt < ntiles) load(nt, k_c);
     lds_barrier();
     f32x4 acc[TP / 16];
     float xh[TP / 16][4];
@@ -805,6 +814,10 @@ __global__ __launch_bounds__(NT) void tm_in_dz_kernel(TmInGradArgs a) {
         *reinterpret_cast<u32x2*>(a.dz + zrow(pair_ix(r, N), N, inc) + c0) =
             u32x2{pack_bf16(dz[0], dz[1]), pack_bf16(dz[2], dz[3])};
     }
+  };
+  for (int tile = blockIdx.x; tile < ntiles; tile += 2 * gs) {
+    body(tile, S0{});
+    if (tile + gs < ntiles) body(tile + gs, S1{});
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
