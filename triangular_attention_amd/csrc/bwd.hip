@@ -37,9 +37,12 @@
 // transposing reads are conflict-free; the score-product row reads of Q, dO
 // and K take two passes.  Swapping the two swizzles removes those conflicts
 // but needs more address registers than the kernel has, and measured slower.
-// The dS^T tile is written 16 bytes per lane and read transposed with a
-// 72-element pitch; the bias tile has 256-byte rows whose 8-byte units are
-// permuted by an XOR with the row's low bits (conflict-free transposing reads).
+// D = 64 (outer group 2, 32-query stages): 128-byte rows whose eight 16-byte
+// chunks are permuted by an XOR with row bits (Q/dO: bits 1, 3, 4; K/V: bits 1, 2,
+// 3) so that both read shapes are conflict-free.  The dS^T tile is written 16
+// bytes per lane and read transposed with a pitch of the stage's queries + 8;
+// the bias tile has 256-byte rows whose 8-byte units are permuted by an XOR with
+// the row's low bits (conflict-free transposing reads).
 #include "common.h"
 #include "kernels.h"
 
