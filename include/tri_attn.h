@@ -65,8 +65,9 @@ typedef enum {
 } tri_attn_status;
 
 /* Problem dimensions.  D must be 16, 32 or 64 (the method is measured at 16 and 32;
- * 64 is a wider head run by the same kernels); B, N_o, H >= 1; 1 <= N <= 32767; scale
- * finite. */
+ * 64 is a wider head run by the same kernels); 1 <= B, N_o, H <= 65535 with
+ * B * N_o <= 65535; 1 <= N <= 32767; B * N_o * H * N <= 2^25; scale finite with
+ * |scale| >= 2^-64 (the backward divides the log-sum-exp by it in FP32). */
 typedef struct {
   int64_t B, N_o, H, N, D;
   float scale;

@@ -36,6 +36,7 @@ class Workload:
     scale: float
     bias_std: float = 1.0
     mask_p: float = 0.0          # Bernoulli probability that a key is masked
+    v_mean: float = 0.0          # mean of the values (V ~ N(v_mean, 1))
     bf16: bool = True            # round Q/K/V/dO/bias to bf16
     description: str = ""
 
@@ -81,6 +82,17 @@ WORKLOADS = {
                                     "per-slice key mask Bernoulli(0.1) additive -1e9, scale 1/sqrt(64)"),
 }
 
+#: Input regimes in which the softmax correction matters (the output-residual ablation): the
+#: headline shape with strongly peaked attention (bias std 4), and with values of mean 2 (the
+#: output is then far from zero while dP - delta, which does not depend on the values' mean,
+#: stays of unit size).
+REGIMES = {
+    "n768_d32_mask_peaked": _w("n768_d32_mask_peaked", 768, 4, 32, 1.0 / math.sqrt(32), mask_p=0.1, bias_std=4.0,
+                               description="as n768_d32_mask with bias N(0, std 4)"),
+    "n768_d32_mask_vmean": _w("n768_d32_mask_vmean", 768, 4, 32, 1.0 / math.sqrt(32), mask_p=0.1, v_mean=2.0,
+                              description="as n768_d32_mask with V ~ N(2, 1)"),
+}
+
 #: The six-shape sweep: crops {384, 640, 768} x head dims {16, 32}, H=4, no mask.
 SWEEP = {f"sweep_n{n}_d{d}": _w(f"sweep_n{n}_d{d}", n, 4, d, 1.0 / math.sqrt(d),
                                 description=f"B=1 N_o=N={n} H=4 D={d} bf16 N(0,1), bias N(0,1), "
@@ -93,6 +105,8 @@ def get(name: str) -> Workload:
         return WORKLOADS[name]
     if name in SWEEP:
         return SWEEP[name]
+    if name in REGIMES:
+        return REGIMES[name]
     raise KeyError(name)
 
 
@@ -110,6 +124,8 @@ def make_inputs(w: Workload, seed: int, bf16: Optional[bool] = None) -> dict:
     q = torch.randn(shp, generator=g, dtype=torch.float32)
     k = torch.randn(shp, generator=g, dtype=torch.float32)
     v = torch.randn(shp, generator=g, dtype=torch.float32)
+    if w.v_mean:
+        v = v + w.v_mean
     do = torch.randn(shp, generator=g, dtype=torch.float32)
     bias = torch.randn((w.B, w.H, w.N, w.N), generator=g, dtype=torch.float32) * w.bias_std
     mask = None
@@ -155,7 +171,8 @@ def make_inputs_device(w: Workload, seed: int, device="cuda") -> dict:
     shp = (w.B, w.N_o, w.H, w.N, w.D)
     out = {}
     for n in ("q", "k", "v", "do"):
-        out[n] = torch.randn(shp, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+        x = torch.randn(shp, generator=g, device=device, dtype=torch.float32)
+        out[n] = (x + w.v_mean if n == "v" and w.v_mean else x).to(torch.bfloat16)
     out["bias"] = (torch.randn((w.B, w.H, w.N, w.N), generator=g, device=device, dtype=torch.float32)
                    * w.bias_std).to(torch.bfloat16)
     out["mask"] = None

@@ -53,3 +53,22 @@ def run_gpu(ta, dev, scale, compensate=True):
 
 def np64(t):
     return t.detach().float().cpu().double().numpy()
+
+
+def row_ratio(got, ref, tol, floor=0.25):
+    """Largest per-row error of ``got`` against ``ref`` (rows = the last axis), in units of ``tol``.
+
+    Each row's error ||g - r|| is divided by the larger of the row's own norm and ``floor``
+    times the RMS row norm of the whole tensor (rows that are nearly zero in the reference,
+    e.g. the key gradients of a masked key, are measured against the typical row), then by
+    ``tol``.  A tensor-level relative RMSE can hide one wrong tile; this cannot: a wrong
+    16 x 16 block gives rows whose error is comparable to their norm.
+    """
+    g = np.asarray(got, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+    r = np.asarray(ref, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+    rn = np.sqrt(np.sum(r * r, axis=1))
+    rms = float(np.sqrt(np.mean(rn * rn)))
+    if rms == 0.0:
+        return float(np.max(np.abs(g))) / tol
+    en = np.sqrt(np.sum((g - r) ** 2, axis=1))
+    return float(np.max(en / np.maximum(rn, floor * rms))) / tol

@@ -64,6 +64,20 @@ def test_validation_errors_before_launch(lib):
     assert _fwd(lib, _dims(B=0)) == 2
     assert _fwd(lib, _dims(scale=float("nan"))) == 2
     assert _fwd(lib, _dims(scale=float("inf"))) == 2
+    # -lse / scale must stay finite in FP32: zero and tiny scales are rejected, 2^-64 is accepted
+    assert _fwd(lib, _dims(scale=0.0)) == 2
+    assert _fwd(lib, _dims(scale=-0.0)) == 2
+    assert _fwd(lib, _dims(scale=1e-30)) == 2
+    assert lib.tri_attn_workspace(ctypes.byref(_dims(scale=2.0 ** -64)), None, None, None, None, None, None) == 0
+    assert lib.tri_attn_workspace(ctypes.byref(_dims(scale=-0.5)), None, None, None, None, None, None) == 0
+    # huge dimensions are rejected before any product of them is formed (no int64 overflow)
+    for big in (2 ** 62, 2 ** 40, 65536):
+        assert _fwd(lib, _dims(B=big)) == 2
+        assert _fwd(lib, _dims(N_o=big)) == 2
+        assert _fwd(lib, _dims(H=big)) == 2
+    assert _fwd(lib, _dims(N=2 ** 62)) == 2
+    assert _fwd(lib, _dims(B=300, N_o=300)) == 2             # B * N_o past the grid limit
+    assert _fwd(lib, _dims(B=1, N_o=4096, H=4096, N=4096)) == 2   # rows past the 32-bit index limit
     assert _fwd(lib, _dims(), q=None) == 1
     assert _fwd(lib, _dims(), lse=None) == 1
     assert _fwd(lib, _dims(), k=MIS) == 4
@@ -186,6 +200,8 @@ def test_block_validation_errors_before_launch(lib):
     assert _ln_proj(lib, _bdims(eps=float("nan"))) == 2
     assert _ln_proj(lib, _bdims(ending=2)) == 2
     assert _ln_proj(lib, _bdims(N=3000)) == 2             # pair tensor past 2^31 bytes
+    assert _ln_proj(lib, _bdims(B=2 ** 62)) == 2          # no int64 overflow in the size check
+    assert _ln_proj(lib, _bdims(B=2 ** 40, N=32767)) == 2
     assert _ln_proj(lib, _bdims(), z=None) == 1
     assert _ln_proj(lib, _bdims(), bias=MIS) == 4
     d = _bdims(H=8, D=16, ending=1)
@@ -240,6 +256,8 @@ def test_trimul_validation_errors_before_launch(lib):
     assert f(_mdims(eps=-1.0)) == 2
     assert f(_mdims(incoming=3)) == 2
     assert f(_mdims(N=1456, c=128)) == 2   # dproj past 2^31 bytes
+    assert f(_mdims(B=2 ** 62)) == 2       # no int64 overflow in the size check
+    assert f(_mdims(B=2 ** 40, N=32760)) == 2
     assert f(_mdims(), z=None) == 1
     assert f(_mdims(), a=MIS) == 4
     d = _mdims(c=64, incoming=1)

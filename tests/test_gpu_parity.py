@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import inputs, np64, require_gpu, run_gpu, to_dev, workload
+from gpu_util import inputs, np64, require_gpu, row_ratio, run_gpu, to_dev, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +61,8 @@ def test_fwd_bwd_matches_oracle(case):
     ref = oracle.backward(x["q"], x["k"], x["v"], x["bias"], x["mask"], w.scale, x["do"])
     e_o = oracle.rel_rmse(np64(got["o"]), ref["o"])
     assert e_o <= TOL_O, e_o
+    # and no single row far off (one wrong tile would not move the tensor-level figure much)
+    assert row_ratio(np64(got["o"]), ref["o"], TOL_O) <= 3.0
     lse_err = np.max(np.abs(np64(got["lse"]) - ref["lse"]))
     assert lse_err <= 1e-3 + 1e-4 * np.max(np.abs(ref["lse"])), lse_err
     # the residual brings the stored output closer to the exact one
@@ -74,6 +76,8 @@ def test_fwd_bwd_matches_oracle(case):
             continue
         e = oracle.rel_rmse(np64(got[n]), ref[n])
         assert e <= TOL_G, (n, e)
+        rr = row_ratio(np64(got[n]), ref[n], TOL_G)
+        assert rr <= 3.0, (n, rr)
     if x["mask"] is not None:
         masked = (x["mask"] < -1e8).numpy()                    # [B, N_o, N]
         mk = np.broadcast_to(masked[:, :, None, :, None], ref["dk"].shape)

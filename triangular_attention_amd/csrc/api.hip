@@ -15,14 +15,18 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 tri_attn_status check_dims(const tri_attn_dims* d) {
   if (!d) return TRI_ATTN_ERR_NULL;
   if (d->B < 1 || d->N_o < 1 || d->H < 1 || d->N < 1 || d->D < 1) return TRI_ATTN_ERR_SHAPE;
-  if (!std::isfinite(d->scale)) return TRI_ATTN_ERR_SHAPE;
+  // the backward forms -lse / scale in FP32: |scale| >= 2^-64 keeps it finite for any
+  // |lse| < 2^63 (zero and subnormal scales are rejected)
+  if (!std::isfinite(d->scale) || std::fabs(d->scale) < 0x1p-64f) return TRI_ATTN_ERR_SHAPE;
   if (d->D != 16 && d->D != 32 && d->D != 64) return TRI_ATTN_ERR_UNSUPPORTED;
-  // 32-bit index limits of the kernels: every per-tensor row count fits in int32 and
-  // the byte size of one FP32 N x N plane (4*N*N) fits in uint32
-  const int64_t rows = d->B * d->N_o * d->H * d->N;
-  if (d->N > (1 << 15) - 1 || rows > (int64_t(1) << 31) / 64 || d->B * d->N_o > kMaxGridZ ||
-      d->H > kMaxGridZ)
+  // each dimension is capped before any product is formed (no int64 overflow); then the
+  // 32-bit index limits of the kernels: every per-tensor row count fits in int32 and the
+  // byte size of one FP32 N x N plane (4*N*N) fits in uint32
+  if (d->N > (1 << 15) - 1 || d->B > kMaxGridZ || d->N_o > kMaxGridZ || d->H > kMaxGridZ)
     return TRI_ATTN_ERR_SHAPE;
+  if (d->B * d->N_o > kMaxGridZ) return TRI_ATTN_ERR_SHAPE;
+  const int64_t rows = d->B * d->N_o * d->H * d->N;     // < 2^16 * 2^16 * 2^15
+  if (rows > (int64_t(1) << 31) / 64) return TRI_ATTN_ERR_SHAPE;
   return TRI_ATTN_OK;
 }
 

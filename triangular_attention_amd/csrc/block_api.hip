@@ -18,7 +18,9 @@ tri_attn_status check(const tri_block_dims* d) {
   if (d->C_z != tri::kBlkC || d->H * d->D != tri::kBlkF || (d->D != 32 && d->D != 16))
     return TRI_ATTN_ERR_UNSUPPORTED;
   // 32-bit element offsets: every pair tensor [B, N, N, 128] must stay below 2^31 bytes
-  if (d->N > 32767 || d->B * d->N * d->N * tri::kBlkC * 2 >= (int64_t(1) << 31)) return TRI_ATTN_ERR_SHAPE;
+  // (B and N are capped first, so the product below cannot overflow int64)
+  if (d->N > 32767 || d->B > 65535 || d->B * d->N * d->N * tri::kBlkC * 2 >= (int64_t(1) << 31))
+    return TRI_ATTN_ERR_SHAPE;
   return TRI_ATTN_OK;
 }
 

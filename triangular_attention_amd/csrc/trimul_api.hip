@@ -19,7 +19,9 @@ tri_attn_status check(const tri_mul_dims* d) {
   if (d->C_z != tri::kTmC || (d->c != 64 && d->c != 128)) return TRI_ATTN_ERR_UNSUPPORTED;
   if (d->N % 8 != 0) return TRI_ATTN_ERR_SHAPE;
   // 32-bit offsets: the largest pair tensor (dproj, [B * N * N, 4c] bf16) stays below 2^31 bytes
-  if (d->N > 32767 || d->B * d->N * d->N * 4 * d->c * 2 >= (int64_t(1) << 31)) return TRI_ATTN_ERR_SHAPE;
+  // (B and N are capped first, so the product below cannot overflow int64)
+  if (d->N > 32767 || d->B > 65535 || d->B * d->N * d->N * 4 * d->c * 2 >= (int64_t(1) << 31))
+    return TRI_ATTN_ERR_SHAPE;
   return TRI_ATTN_OK;
 }
 
