@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-compensate", action="store_true", help="run without the output residual")
     ap.add_argument("--partials", choices=("fp32", "bf16"), default="fp32",
                     help="partial precision: fp32 (the reference contract) or the bf16-partial variant")
+    ap.add_argument("--chunk-groups", type=int, default=0,
+                    help="run the backward as tri_attn_bwd_chunked with chunks of this many outer groups "
+                         "(bounded partial memory); 0 = the unchunked calls")
     ap.add_argument("--cpu-seconds", type=float, default=25.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -235,8 +238,19 @@ def main():
         "reduce_dbias": lambda: ta.tri_attn_reduce_dbias(d, dbp, dbias, stream, bf16_partials=bp),
     }
 
+    names = KERNELS
+    if args.chunk_groups > 0:
+        if bp:
+            raise SystemExit("--chunk-groups runs FP32 partials only")
+        del dqp, dbp
+        cw = ta.chunked_workspace(d, args.chunk_groups)
+        cbuf = torch.empty(cw["bytes"], dtype=torch.uint8, device=dev)
+        calls["bwd_chunked"] = lambda: ta.tri_attn_bwd_chunked(d, q, k, v, bias, mask, do, lse, delta, dq, dk, dv,
+                                                              dbias, cbuf, stream)
+        names = ("fwd", "delta", "bwd_chunked")
+
     def step():
-        for n in KERNELS:
+        for n in names:
             calls[n]()
 
     for _ in range(args.warmup):
@@ -257,26 +271,28 @@ def main():
     ms_step = ms_total / args.steps
 
     # per-kernel durations: events on the launch stream around each kernel, K more steps
-    per = {n: 0.0 for n in KERNELS}
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
+    per = {n: 0.0 for n in names}
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     for s in range(args.steps):
         evs[s][0].record(stream)
-        for i, n in enumerate(KERNELS):
+        for i, n in enumerate(names):
             calls[n]()
             evs[s][i + 1].record(stream)
     torch.cuda.synchronize()
     for s in range(args.steps):
-        for i, n in enumerate(KERNELS):
+        for i, n in enumerate(names):
             per[n] += evs[s][i].elapsed_time(evs[s][i + 1]) / args.steps
 
     alg = algorithmic(w, ws["j_k"], ws["l"], 2 if bp else 4)
+    # the chunked call does the work of the main backward and both reductions
+    alg["bwd_chunked"] = {k: alg["bwd"][k] + alg["reduce_dq"][k] + alg["reduce_dbias"][k] for k in ("flops", "bytes")}
     kernels = {}
-    for n in KERNELS:
+    for n in names:
         ms = per[n]
         kernels[n] = {"ms": round(ms, 5),
                       "tflops": round(alg[n]["flops"] / (ms * 1e-3) / 1e12, 2) if ms > 0 else None,
                       "alg_gbs": round(alg[n]["bytes"] / (ms * 1e-3) / 1e9, 1) if ms > 0 else None}
-    dom = max(KERNELS, key=lambda n: per[n])
+    dom = max(names, key=lambda n: per[n])
     traffic = None
     traffic_all = None
     if os.path.exists(args.traffic):
@@ -323,6 +339,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "N_o": w.N_o, "N": w.N, "H": w.H, "D": w.D,
                    "scale": w.scale, "bias_std": w.bias_std, "mask_p": w.mask_p,
                    "compensate": comp, "partials": args.partials, "flops_per_step": w.flops_fwd_bwd,
+                   **({"chunk_groups": cw["groups_per_chunk"], "chunk_workspace_bytes": cw["bytes"]}
+                      if args.chunk_groups > 0 else {}),
                    "key_tile": ws["key_tile"], "outer_group": ws["outer_group"],
                    "description": w.description},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

@@ -34,7 +34,8 @@
  * Errors: arguments are checked on the host before any launch.  A null
  * required pointer gives TRI_ATTN_ERR_NULL, a bad dimension or scale
  * TRI_ATTN_ERR_SHAPE, an unsupported head dimension TRI_ATTN_ERR_UNSUPPORTED,
- * a pointer not 16-byte aligned TRI_ATTN_ERR_ALIGN, and a failed launch
+ * a pointer not 16-byte aligned TRI_ATTN_ERR_ALIGN, a workspace too small for
+ * the chunked backward TRI_ATTN_ERR_WORKSPACE, and a failed launch
  * TRI_ATTN_ERR_LAUNCH; in every error case nothing has been enqueued except
  * for TRI_ATTN_ERR_LAUNCH.  Device faults surface at the caller's next
  * synchronisation, as for any HIP call.  NaN and Inf inputs propagate; bias
@@ -61,7 +62,8 @@ typedef enum {
   TRI_ATTN_ERR_SHAPE = 2,
   TRI_ATTN_ERR_UNSUPPORTED = 3,
   TRI_ATTN_ERR_ALIGN = 4,
-  TRI_ATTN_ERR_LAUNCH = 5
+  TRI_ATTN_ERR_LAUNCH = 5,
+  TRI_ATTN_ERR_WORKSPACE = 6
 } tri_attn_status;
 
 /* Problem dimensions.  D must be 16, 32 or 64 (the method is measured at 16 and 32;
@@ -145,6 +147,40 @@ tri_attn_status tri_attn_reduce_dq_bf16p(const tri_attn_dims* d, const tri_bf16*
                                          tri_bf16* dq, tri_attn_stream stream);
 tri_attn_status tri_attn_reduce_dbias_bf16p(const tri_attn_dims* d, const tri_bf16* dbias_partial,
                                             tri_bf16* dbias, tri_attn_stream stream);
+
+/*
+ * Chunked backward with bounded partial memory (Figure 7(d): the pair-bias partial
+ * buffers are reused once consumed; Table 2, column W_bias,res).  Does what
+ * tri_attn_bwd, tri_attn_reduce_dq and tri_attn_reduce_dbias do together, over chunks of
+ * C consecutive outer groups: the main backward of a chunk writes the chunk's dQ and
+ * dbias partials into `workspace`, then one reduction kernel sums the chunk's dQ
+ * partials into its rows of dq and adds its dbias partials, in ascending group order, to
+ * an FP32 running sum carried from chunk to chunk (rounded to bf16 into dbias after the
+ * last chunk); the next chunk reuses the same buffers.  Every sum keeps the order of the
+ * unchunked calls, so dq, dk, dv and dbias are bitwise those of the three calls.
+ *
+ * C is the largest number of outer groups whose buffers fit in workspace_bytes (all
+ * groups: a single chunk).  tri_attn_bwd_chunked_workspace gives the bytes a chunk of
+ * groups_per_chunk groups needs (clamped to 1..L) and the clamped count.  Buffers of one
+ * chunk: dQ partials J_K * B * min(C * G, N_o) * H * N * D FP32, dbias partials
+ * C * B * H * N * N FP32, and with more than one chunk the running sum B * H * N * N FP32
+ * (each rounded up to 256 bytes).
+ *
+ * Inputs and dq, dk, dv, dbias as for the three calls; `workspace` is caller-owned device
+ * memory, 16-byte aligned, whose contents on entry do not matter and which no other call
+ * may use until this call's kernels have finished.  Errors as for tri_attn_bwd, plus
+ * TRI_ATTN_ERR_NULL for a null workspace and TRI_ATTN_ERR_WORKSPACE when not even one
+ * outer group's buffers fit in workspace_bytes.
+ */
+tri_attn_status tri_attn_bwd_chunked_workspace(const tri_attn_dims* d, int64_t groups_per_chunk,
+                                               int64_t* workspace_bytes, int64_t* groups_used);
+tri_attn_status tri_attn_bwd_chunked(const tri_attn_dims* d,
+                                     const tri_bf16* q, const tri_bf16* k, const tri_bf16* v,
+                                     const tri_bf16* bias, const float* mask /* may be NULL */,
+                                     const tri_bf16* d_o, const float* lse, const float* delta,
+                                     tri_bf16* dq, tri_bf16* dk, tri_bf16* dv, tri_bf16* dbias,
+                                     void* workspace, int64_t workspace_bytes,
+                                     tri_attn_stream stream);
 
 /*
  * Partial-buffer sizes for these dimensions (elements, FP32), the number of

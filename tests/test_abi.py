@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert lib.tri_attn_status_string(code)
     assert lib.tri_attn_status_string(99) == b"unknown status"
 
@@ -283,3 +283,52 @@ def test_trimul_workspace_counts(lib, B, N, c):
     assert vals[1].value == min(-(-pairs // 64), 256)
     assert vals[2].value == min(-(-pairs // 32), 256)
     assert vals[3].value == vals[1].value * (128 // c)
+
+
+# --------------------------------------------------------------------------- chunked backward
+
+
+def _chunked(lib, d, ws=P, nbytes=1 << 40, **ptrs):
+    names = ("q", "k", "v", "bias", "mask", "d_o", "lse", "delta", "dq", "dk", "dv", "dbias")
+    a = {n: P for n in names}
+    a["mask"] = None
+    a.update(ptrs)
+    return lib.tri_attn_bwd_chunked(None if d is None else ctypes.byref(d), *[a[n] for n in names], ws, nbytes, None)
+
+
+def test_chunked_validation_errors_before_launch(lib):
+    d = _dims(N_o=10, N=100)
+    assert _chunked(lib, None) == 1
+    assert _chunked(lib, d, ws=None) == 1
+    assert _chunked(lib, d, dbias=None) == 1
+    assert _chunked(lib, d, ws=MIS) == 4
+    assert _chunked(lib, d, dq=MIS) == 4
+    assert _chunked(lib, _dims(D=48)) == 3
+    assert _chunked(lib, _dims(scale=0.0)) == 2
+    need = ctypes.c_int64()
+    assert lib.tri_attn_bwd_chunked_workspace(ctypes.byref(d), 1, ctypes.byref(need), None) == 0
+    assert _chunked(lib, d, nbytes=need.value - 1) == 6        # not even one outer group fits
+    assert _chunked(lib, d, nbytes=0) == 6
+    assert lib.tri_attn_bwd_chunked_workspace(ctypes.byref(d), 0, ctypes.byref(need), None) == 2
+
+
+@pytest.mark.parametrize("B,N_o,H,N,D", [(1, 768, 4, 768, 32), (2, 13, 3, 100, 16), (1, 9, 2, 67, 64),
+                                         (3, 5, 1, 33, 32)])
+def test_chunked_workspace_sizes(lib, B, N_o, H, N, D):
+    """Bytes of one chunk of C outer groups: dQ partials J_K * B * min(C * G, N_o) * H * N * D, dbias
+    partials C * B * H * N * N and, when there is more than one chunk, the running dbias sum
+    B * H * N * N, all FP32 and each rounded up to 256 bytes; C is clamped to 1..L."""
+    from triangular_attention_amd import api
+    d = _dims(B=B, N_o=N_o, H=H, N=N, D=D)
+    ws = api.workspace(d)
+    G, L, jk = ws["outer_group"], ws["l"], ws["j_k"]
+    up = lambda x: -(-x // 256) * 256
+    for C in (1, 2, 3, L - 1, L, L + 5):
+        if C < 1:
+            continue
+        Cc = min(C, L)
+        chunks = -(-L // Cc)
+        want = up(4 * jk * B * min(Cc * G, N_o) * H * N * D) + up(4 * Cc * B * H * N * N) + \
+            (up(4 * B * H * N * N) if chunks > 1 else 0)
+        got = api.chunked_workspace(d, C)
+        assert got == {"bytes": want, "groups_per_chunk": Cc}, (C, got, want)

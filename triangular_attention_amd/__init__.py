@@ -12,9 +12,12 @@ offers ``triangle_multiplication``.
 from ._lib import BLOCK_EXPORTS, EXPORTS, LIB_PATH, TRIMUL_EXPORTS, BlockDims, Dims, MulDims, TriAttnError, load  # noqa: F401
 from .api import (  # noqa: F401
     backward,
+    backward_chunked,
+    chunked_workspace,
     dims_of,
     forward,
     tri_attn_bwd,
+    tri_attn_bwd_chunked,
     tri_attn_bwd_delta,
     tri_attn_fwd,
     tri_attn_reduce_dbias,

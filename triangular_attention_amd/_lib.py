@@ -20,6 +20,7 @@ STATUS = {
     3: "TRI_ATTN_ERR_UNSUPPORTED",
     4: "TRI_ATTN_ERR_ALIGN",
     5: "TRI_ATTN_ERR_LAUNCH",
+    6: "TRI_ATTN_ERR_WORKSPACE",
 }
 
 #: every symbol include/tri_attn.h declares
@@ -32,6 +33,8 @@ EXPORTS = (
     "tri_attn_bwd_bf16p",
     "tri_attn_reduce_dq_bf16p",
     "tri_attn_reduce_dbias_bf16p",
+    "tri_attn_bwd_chunked_workspace",
+    "tri_attn_bwd_chunked",
     "tri_attn_workspace",
     "tri_attn_status_string",
     "tri_attn_version",
@@ -131,6 +134,8 @@ def load() -> ctypes.CDLL:
         "tri_attn_reduce_dq_bf16p": [dp, vp, vp, vp],
         "tri_attn_reduce_dbias_bf16p": [dp, vp, vp, vp],
         "tri_attn_workspace": [dp, i64p, i64p, i64p, i64p, i64p, i64p],
+        "tri_attn_bwd_chunked_workspace": [dp, ctypes.c_int64, i64p, i64p],
+        "tri_attn_bwd_chunked": [dp] + [vp] * 13 + [ctypes.c_int64, vp],
     }
     bp = ctypes.POINTER(BlockDims)
     sig.update({

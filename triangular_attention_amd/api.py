@@ -140,6 +140,40 @@ def tri_attn_reduce_dbias(d, dbias_partial, dbias, stream=None, bf16_partials=Fa
     _lib.check(name, getattr(lib, name)(ctypes.byref(d), _ptr(dbias_partial), _ptr(dbias), _stream(stream)))
 
 
+def chunked_workspace(d, groups_per_chunk: int) -> dict:
+    """Bytes the chunked backward needs for chunks of ``groups_per_chunk`` outer groups
+    (``tri_attn_bwd_chunked_workspace``); host-only."""
+    lib = _lib.load()
+    nbytes, used = ctypes.c_int64(), ctypes.c_int64()
+    _lib.check("tri_attn_bwd_chunked_workspace",
+               lib.tri_attn_bwd_chunked_workspace(ctypes.byref(d), int(groups_per_chunk), ctypes.byref(nbytes),
+                                                  ctypes.byref(used)))
+    return {"bytes": nbytes.value, "groups_per_chunk": used.value}
+
+
+def tri_attn_bwd_chunked(d, q, k, v, bias, mask, d_o, lse, delta, dq, dk, dv, dbias, workspace, stream=None):
+    """Chunked backward (main backward + both reductions over chunks of outer groups whose
+    partials fit in ``workspace``, a uint8 device tensor)."""
+    B, N_o, H, N, D = d.B, d.N_o, d.H, d.N, d.D
+    x = (B, N_o, H, N, D)
+    for n, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, n, torch.bfloat16, x)
+    for n, t in (("bias", bias), ("dbias", dbias)):
+        _need(t, n, torch.bfloat16, (B, H, N, N))
+    if mask is not None:
+        _need(mask, "mask", torch.float32, (B, N_o, N))
+    _need(lse, "lse", torch.float32, (B, N_o, H, N))
+    _need(delta, "delta", torch.float32, (B, N_o, H, N))
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or not workspace.is_cuda \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    lib = _lib.load()
+    _lib.check("tri_attn_bwd_chunked",
+               lib.tri_attn_bwd_chunked(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
+                                        _ptr(d_o), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+                                        _ptr(dbias), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
 # --------------------------------------------------------------------------- composite calls
 
 
@@ -175,6 +209,21 @@ def backward(q, k, v, bias, mask, scale, o, o_res, lse, d_o, workspace_buffers=N
     # better after the dbias reduction than straight after the backward)
     tri_attn_reduce_dbias(d, db_part, dbias, bf16_partials=bf16_partials)
     tri_attn_reduce_dq(d, dq_part, dq, bf16_partials=bf16_partials)
+    return dq, dk, dv, dbias
+
+
+def backward_chunked(q, k, v, bias, mask, scale, o, o_res, lse, d_o, groups_per_chunk=None, buffer=None):
+    """Delta, then the chunked backward (bounded partial memory).  The workspace ``buffer``
+    (uint8 device tensor) is allocated for ``groups_per_chunk`` outer groups (all groups when
+    None) unless one is given.  Returns ``(dq, dk, dv, dbias)``, bitwise those of ``backward``."""
+    d = dims_of(q, scale)
+    if buffer is None:
+        n = workspace(d)["l"] if groups_per_chunk is None else groups_per_chunk
+        buffer = torch.empty(chunked_workspace(d, n)["bytes"], dtype=torch.uint8, device=q.device)
+    delta = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    tri_attn_bwd_delta(d, o, o_res, d_o, delta)
+    dq, dk, dv, dbias = (torch.empty_like(t) for t in (q, k, v, bias))
+    tri_attn_bwd_chunked(d, q, k, v, bias, mask, d_o, lse, delta, dq, dk, dv, dbias, buffer)
     return dq, dk, dv, dbias
 
 

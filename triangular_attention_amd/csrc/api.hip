@@ -1,5 +1,6 @@
 // C ABI of the triangular-attention library: argument validation and launch.
 // See include/tri_attn.h for the contract of each entry point.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -50,6 +51,7 @@ const char* tri_attn_status_string(tri_attn_status s) {
     case TRI_ATTN_ERR_UNSUPPORTED: return "unsupported head dimension (D must be 16, 32 or 64)";
     case TRI_ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
     case TRI_ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case TRI_ATTN_ERR_WORKSPACE: return "workspace too small for the partials of one outer group";
   }
   return "unknown status";
 }
@@ -105,6 +107,36 @@ tri_attn_status tri_attn_bwd_delta(const tri_attn_dims* d, const tri_bf16* o,
 
 namespace {
 
+// Arguments of the backward kernel over every outer group (no partial buffers yet).
+tri::BwdArgs bwd_args(const tri_attn_dims* d, const tri_bf16* q, const tri_bf16* k, const tri_bf16* v,
+                      const tri_bf16* bias, const float* mask, const tri_bf16* d_o, const float* lse,
+                      const float* delta, tri_bf16* dk, tri_bf16* dv) {
+  tri::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.bias = bias; a.mask = mask; a.d_o = d_o;
+  a.lse = lse; a.delta = delta; a.dk = dk; a.dv = dv;
+  a.dq_partial = nullptr; a.dbias_partial = nullptr;
+  a.bf16_partials = 0;
+  a.B = (int)d->B; a.N_o = (int)d->N_o; a.H = (int)d->H; a.N = (int)d->N;
+  a.n_key_tiles = (int)n_key_tiles(d);
+  a.g0 = 0;
+  a.n_groups = (int)n_groups(d);
+  a.part_slices = (int)d->N_o;
+  a.scale = d->scale;
+  return a;
+}
+
+tri_attn_status check_bwd_inputs(const tri_attn_dims* d, const tri_bf16* q, const tri_bf16* k,
+                                 const tri_bf16* v, const tri_bf16* bias, const float* mask,
+                                 const tri_bf16* d_o, const float* lse, const float* delta) {
+  if (!q || !k || !v || !bias || !d_o || !lse || !delta) return TRI_ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bias) || !aligned16(d_o) ||
+      !aligned16(lse) || !aligned16(delta) || (mask && !aligned16(mask)))
+    return TRI_ATTN_ERR_ALIGN;
+  // a launch has 8 * ceil(B * L * H / 8) * J_K workgroups (32-bit grid)
+  if (n_key_tiles(d) * (d->H * n_groups(d) * d->B + 7) > 0x7fffffff) return TRI_ATTN_ERR_SHAPE;
+  return TRI_ATTN_OK;
+}
+
 tri_attn_status bwd_impl(const tri_attn_dims* d, const tri_bf16* q, const tri_bf16* k,
                          const tri_bf16* v, const tri_bf16* bias, const float* mask,
                          const tri_bf16* d_o, const float* lse, const float* delta, tri_bf16* dk,
@@ -112,25 +144,117 @@ tri_attn_status bwd_impl(const tri_attn_dims* d, const tri_bf16* q, const tri_bf
                          tri_attn_stream stream) {
   tri_attn_status st = check_dims(d);
   if (st != TRI_ATTN_OK) return st;
-  if (!q || !k || !v || !bias || !d_o || !lse || !delta || !dk || !dv || !dq_partial ||
-      !dbias_partial)
-    return TRI_ATTN_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bias) || !aligned16(d_o) ||
-      !aligned16(lse) || !aligned16(delta) || !aligned16(dk) || !aligned16(dv) ||
-      !aligned16(dq_partial) || !aligned16(dbias_partial) || (mask && !aligned16(mask)))
+  if (!dk || !dv || !dq_partial || !dbias_partial) return TRI_ATTN_ERR_NULL;
+  st = check_bwd_inputs(d, q, k, v, bias, mask, d_o, lse, delta);
+  if (st != TRI_ATTN_OK) return st;
+  if (!aligned16(dk) || !aligned16(dv) || !aligned16(dq_partial) || !aligned16(dbias_partial))
     return TRI_ATTN_ERR_ALIGN;
-  tri::BwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.bias = bias; a.mask = mask; a.d_o = d_o;
-  a.lse = lse; a.delta = delta; a.dk = dk; a.dv = dv;
+  tri::BwdArgs a = bwd_args(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv);
   a.dq_partial = dq_partial; a.dbias_partial = dbias_partial;
   a.bf16_partials = bf16_partials;
-  a.B = (int)d->B; a.N_o = (int)d->N_o; a.H = (int)d->H; a.N = (int)d->N;
-  a.n_key_tiles = (int)n_key_tiles(d);
-  a.n_groups = (int)n_groups(d);
-  a.scale = d->scale;
-  const int64_t nblk = n_key_tiles(d) * d->H * n_groups(d) * d->B;
-  if (nblk > 0x7fffffff) return TRI_ATTN_ERR_SHAPE;
   return launched(tri::launch_bwd(a, (int)d->D, (hipStream_t)stream));
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+// Buffers of the chunked backward for chunks of C outer groups, as byte offsets into the
+// workspace: the chunk's dQ partials [J_K, B, PS, H, N, D] (PS = min(C * G, N_o) slices per
+// example), its dbias partials [C, B, H, N, N], and the FP32 running dbias sum [B, H, N, N]
+// (only with more than one chunk).
+struct ChunkPlan {
+  int64_t C = 0, n_chunks = 0, part_slices = 0;
+  int64_t dq_off = 0, db_off = 0, acc_off = 0, bytes = 0;
+};
+
+ChunkPlan chunk_plan(const tri_attn_dims* d, int64_t C) {
+  const int64_t L = n_groups(d), G = group_size(d);
+  ChunkPlan p;
+  p.C = std::max<int64_t>(1, std::min(C, L));
+  p.n_chunks = (L + p.C - 1) / p.C;
+  p.part_slices = std::min(p.C * G, d->N_o);
+  const int64_t dq = 4 * n_key_tiles(d) * d->B * p.part_slices * d->H * d->N * d->D;
+  const int64_t db = 4 * p.C * y_elems(d);
+  const int64_t acc = p.n_chunks > 1 ? 4 * y_elems(d) : 0;
+  p.dq_off = 0;
+  p.db_off = align256(dq);
+  p.acc_off = p.db_off + align256(db);
+  p.bytes = p.acc_off + align256(acc);
+  return p;
+}
+
+// The largest chunk whose buffers fit in `bytes` (C = 0: not even one outer group fits).
+ChunkPlan chunk_plan_for(const tri_attn_dims* d, int64_t bytes) {
+  for (int64_t C = n_groups(d); C >= 1; --C) {
+    const ChunkPlan p = chunk_plan(d, C);
+    if (p.bytes <= bytes) return p;
+  }
+  return ChunkPlan();
+}
+
+// Backward over chunks of outer groups (see tri_attn_bwd_chunked): per chunk, the main
+// backward writes the chunk's partials, then one launch of the segmented reduction forms the
+// chunk's dQ rows and carries the dbias sum on; the next chunk reuses the buffers.
+tri_attn_status chunked_impl(const tri_attn_dims* d, const tri_bf16* q, const tri_bf16* k,
+                             const tri_bf16* v, const tri_bf16* bias, const float* mask,
+                             const tri_bf16* d_o, const float* lse, const float* delta, tri_bf16* dq,
+                             tri_bf16* dk, tri_bf16* dv, tri_bf16* dbias, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream) {
+  tri_attn_status st = check_dims(d);
+  if (st != TRI_ATTN_OK) return st;
+  if (!dq || !dk || !dv || !dbias || !workspace) return TRI_ATTN_ERR_NULL;
+  st = check_bwd_inputs(d, q, k, v, bias, mask, d_o, lse, delta);
+  if (st != TRI_ATTN_OK) return st;
+  if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dbias) || !aligned16(workspace))
+    return TRI_ATTN_ERR_ALIGN;
+  const ChunkPlan plan = chunk_plan_for(d, workspace_bytes);
+  if (plan.C == 0) return TRI_ATTN_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* dqp = reinterpret_cast<float*>(ws + plan.dq_off);
+  float* dbp = reinterpret_cast<float*>(ws + plan.db_off);
+  float* acc = reinterpret_cast<float*>(ws + plan.acc_off);
+  tri::BwdArgs a = bwd_args(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv);
+  a.dq_partial = dqp;
+  a.dbias_partial = dbp;
+  a.part_slices = (int)plan.part_slices;
+  const int64_t L = n_groups(d), G = group_size(d), PS = plan.part_slices;
+  const int64_t slice = d->H * d->N * d->D;     // elements of one outer slice of Q
+  for (int64_t c = 0; c < plan.n_chunks; ++c) {
+    const int64_t g0 = c * plan.C, ng = std::min(plan.C, L - g0);
+    a.g0 = (int)g0;
+    a.n_groups = (int)ng;
+    hipError_t e = tri::launch_bwd(a, (int)d->D, stream);
+    if (e != hipSuccess) return TRI_ATTN_ERR_LAUNCH;
+    const int64_t s0 = g0 * G, ns = std::min(d->N_o, (g0 + ng) * G) - s0;
+    tri::SegReduceArgs r;
+    r.njobs = 2;
+    // the dbias job first: its blocks each add a chunk's worth of partials and run longest,
+    // so they start first and the short dQ blocks fill in behind them
+    tri::SegReduceJob& jq = r.job[1];     // the chunk's dQ rows: sum over key tiles
+    jq.partial = dqp;
+    jq.pstride = d->B * PS * slice;
+    jq.sstride = PS * slice;
+    jq.seg_len = ns * slice;
+    jq.nseg = (int)d->B;
+    jq.n_partials = (int)n_key_tiles(d);
+    jq.acc_in = nullptr;
+    jq.acc_out = nullptr;
+    jq.out = dq + s0 * slice;
+    jq.ostride = d->N_o * slice;
+    tri::SegReduceJob& jb = r.job[0];     // dbias: the running sum over outer groups
+    jb.partial = dbp;
+    jb.pstride = y_elems(d);
+    jb.sstride = 0;
+    jb.seg_len = y_elems(d);
+    jb.nseg = 1;
+    jb.n_partials = (int)ng;
+    jb.acc_in = c > 0 ? acc : nullptr;
+    jb.acc_out = c + 1 < plan.n_chunks ? acc : nullptr;
+    jb.out = dbias;
+    jb.ostride = 0;
+    e = tri::launch_seg_reduce(r, stream);
+    if (e != hipSuccess) return TRI_ATTN_ERR_LAUNCH;
+  }
+  return TRI_ATTN_OK;
 }
 
 tri_attn_status reduce_impl(const tri_attn_dims* d, const void* partial, tri_bf16* out, bool dq,
@@ -185,6 +309,26 @@ tri_attn_status tri_attn_reduce_dq_bf16p(const tri_attn_dims* d, const tri_bf16*
 tri_attn_status tri_attn_reduce_dbias_bf16p(const tri_attn_dims* d, const tri_bf16* dbias_partial,
                                             tri_bf16* dbias, tri_attn_stream stream) {
   return reduce_impl(d, dbias_partial, dbias, false, 1, stream);
+}
+
+tri_attn_status tri_attn_bwd_chunked_workspace(const tri_attn_dims* d, int64_t groups_per_chunk,
+                                               int64_t* workspace_bytes, int64_t* groups_used) {
+  tri_attn_status st = check_dims(d);
+  if (st != TRI_ATTN_OK) return st;
+  if (groups_per_chunk < 1) return TRI_ATTN_ERR_SHAPE;
+  const ChunkPlan p = chunk_plan(d, groups_per_chunk);
+  if (workspace_bytes) *workspace_bytes = p.bytes;
+  if (groups_used) *groups_used = p.C;
+  return TRI_ATTN_OK;
+}
+
+tri_attn_status tri_attn_bwd_chunked(const tri_attn_dims* d, const tri_bf16* q, const tri_bf16* k,
+                                     const tri_bf16* v, const tri_bf16* bias, const float* mask,
+                                     const tri_bf16* d_o, const float* lse, const float* delta,
+                                     tri_bf16* dq, tri_bf16* dk, tri_bf16* dv, tri_bf16* dbias,
+                                     void* workspace, int64_t workspace_bytes, tri_attn_stream stream) {
+  return chunked_impl(d, q, k, v, bias, mask, d_o, lse, delta, dq, dk, dv, dbias, workspace, workspace_bytes,
+                      (hipStream_t)stream);
 }
 
 }  // extern "C"

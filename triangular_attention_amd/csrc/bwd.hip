@@ -175,14 +175,15 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   // XCD-aware order: blocks are dispatched round-robin over 8 XCDs; the key
   // tiles of one (example, group, head) unit run on the same XCD so that they
   // share its L2 for Q, dO and the bias rows.
-  const int nunit = a.B * a.n_groups * H;
+  const int nunit = a.B * a.n_groups * H;     // groups of this launch (all, or one chunk)
   const int per_xcd = (nunit + 7) / 8;
   const int xcd = blockIdx.x % 8, kx = blockIdx.x / 8;
   const int unit = (kx / a.n_key_tiles) * 8 + xcd;
   if (kx / a.n_key_tiles >= per_xcd || unit >= nunit) return;
   const int t = kx % a.n_key_tiles;
   const int h = unit % H;
-  const int grp = (unit / H) % a.n_groups;
+  const int grp_l = (unit / H) % a.n_groups;   // group index within the launch
+  const int grp = a.g0 + grp_l;                 // outer group: slices grp*G ..
   const int b = unit / (H * a.n_groups);
 
   const float scale = a.scale;
@@ -201,7 +202,10 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   // rows of slice (b, grp*G + gs, h) start at row0 + gs * ostride in the [B, N_o, H, N] row space
   const int64_t row0 = (((int64_t)b * N_o + grp * G) * H + h) * N;
   const int64_t ostride = (int64_t)H * N;
-  const int64_t part_rows = (int64_t)a.B * N_o * H * N;    // rows of one dQ partial
+  // dQ partials hold a.part_slices slices per example (N_o, or the slices of one chunk);
+  // the launch's group grp_l starts at slice grp_l * G of them
+  const int64_t part_rows = (int64_t)a.B * a.part_slices * H * N;    // rows of one dQ partial
+  const int64_t prow0 = (((int64_t)b * a.part_slices + grp_l * G) * H + h) * N;
   const uint32_t rowbytes = (uint32_t)N * D * 2;
   auto srow = [&](int gs) { return row0 + (gs < nsl ? gs : 0) * ostride; };
   const uint16_t* bias_plane = a.bias + ((int64_t)b * H + h) * N * N;
@@ -441,7 +445,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         if (st & 1) dq1 = mfma_k32(ak[st], bs[st], dq1);
         else dq0 = mfma_k32(ak[st], bs[st], dq0);
       }
-      const int64_t prow = t * part_rows + srow(gg) + (int64_t)jj * TQ;
+      const int64_t prow = t * part_rows + prow0 + (gg < nsl ? gg : 0) * ostride + (int64_t)jj * TQ;
       const f32x4 v = (dq0 + dq1) * scale;
       if constexpr (BP) {   // bf16 partials: one RNE rounding, 8 bytes per lane
         const uint32_t ext = __builtin_amdgcn_readfirstlane(store && gg < nsl ? (uint32_t)(N - jj * TQ) * D * 2 : 0u);
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     if (kok) {
       // this group's dbias partial for (query tile j, key tile t); in the last query
       // tile rows past N go to an offset past the plane's extent and are dropped
-      const int64_t plane = (((int64_t)grp * a.B + b) * H + h) * N * N;
+      const int64_t plane = (((int64_t)grp_l * a.B + b) * H + h) * N * N;
       constexpr int EB = BP ? 2 : 4;         // bytes per partial element
       const __amdgpu_buffer_rsrc_t rs =
           BP ? make_rsrc((uint16_t*)a.dbias_partial + plane, (uint32_t)N * N * 2)

@@ -8,6 +8,8 @@
 // single-writer partials in ascending index order in FP32 (FP32 partials, or
 // bf16 partials as the pages' Table 2 sizes them).
 // All three are HBM-bound: coalesced 16-byte loads, no LDS.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -125,6 +127,59 @@ __global__ __launch_bounds__(256) void reduce_bf16_kernel(ReduceArgs a) {
   }
 }
 
+// Segmented sums for the chunked backward: the same ascending order as reduce_kernel,
+// optionally continuing an FP32 running sum carried over from earlier chunks, so that the
+// chunked result is bitwise the unchunked one.  VEC: four consecutive elements per thread
+// (16-byte loads); otherwise one element per thread.  Blocks [0, job[0].blocks) serve job 0,
+// the rest job 1.
+template <bool VEC>
+__global__ __launch_bounds__(256) void seg_reduce_kernel(SegReduceArgs a) {
+  constexpr int EPT = VEC ? 4 : 1;
+  constexpr int U = 8;            // partials per batch of loads
+  int64_t blk = blockIdx.x;
+  const int j = blk < a.job[0].blocks ? 0 : 1;
+  if (j == 1) blk -= a.job[0].blocks;
+  const SegReduceJob jb = j == 0 ? a.job[0] : a.job[1];
+  // whole blocks per segment: the segment and the offset in it come from the (uniform)
+  // block index, no per-lane 64-bit division
+  const int64_t bps = (jb.seg_len + 256 * EPT - 1) / (256 * EPT);
+  const int64_t sg = blk / bps;
+  const int64_t i = (blk - sg * bps) * 256 * EPT + threadIdx.x * EPT;
+  if (i >= jb.seg_len) return;
+  const int64_t e0 = sg * jb.seg_len + i;     // element of the dense running sum
+  const float* src = jb.partial + sg * jb.sstride + i;
+  typedef typename std::conditional<VEC, f32x4, float>::type V;
+  auto ld = [&](const float* p) -> V {
+    if constexpr (VEC) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    else return __builtin_nontemporal_load(p);
+  };
+  V acc;
+  const bool carry = jb.acc_in != nullptr;
+  if (carry) {
+    if constexpr (VEC) acc = *reinterpret_cast<const f32x4*>(jb.acc_in + e0);
+    else acc = jb.acc_in[e0];
+  }
+  for (int p = 0; p < jb.n_partials; p += U) {
+    V x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (p + u < jb.n_partials) x[u] = ld(src + (int64_t)(p + u) * jb.pstride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (p + u == 0 && !carry) acc = x[u];
+      else if (p + u < jb.n_partials) acc += x[u];
+    }
+  }
+  if (jb.acc_out) {
+    if constexpr (VEC) *reinterpret_cast<f32x4*>(jb.acc_out + e0) = acc;
+    else jb.acc_out[e0] = acc;
+  } else {
+    uint16_t* o = jb.out + sg * jb.ostride + i;
+    if constexpr (VEC) *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+    else *o = f_to_bf(acc);
+  }
+}
+
 template <int D, bool RES>
 static hipError_t launch_delta_t(const DeltaArgs& a, hipStream_t s) {
   const int64_t threads = a.rows * (D / 8);
@@ -151,6 +206,26 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
   const int64_t threads = (a.elems + EPT - 1) / EPT;
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL(reduce_kernel<EPT>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_reduce(SegReduceArgs a, hipStream_t s) {
+  bool vec = true;
+  for (int j = 0; j < a.njobs; ++j) {
+    const SegReduceJob& jb = a.job[j];
+    vec = vec && jb.seg_len % 4 == 0 && jb.pstride % 4 == 0 && jb.sstride % 4 == 0 && jb.ostride % 4 == 0;
+  }
+  int64_t total = 0;
+  for (int j = 0; j < 2; ++j) {
+    SegReduceJob& jb = a.job[j];
+    jb.vec = vec;
+    const int64_t per_block = 256 * (vec ? 4 : 1);
+    jb.blocks = j < a.njobs ? jb.nseg * ((jb.seg_len + per_block - 1) / per_block) : 0;
+    total += jb.blocks;
+  }
+  if (total == 0) return hipSuccess;
+  if (vec) hipLaunchKernelGGL(seg_reduce_kernel<true>, dim3((unsigned)total), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(seg_reduce_kernel<false>, dim3((unsigned)total), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

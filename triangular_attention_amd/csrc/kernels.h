@@ -58,7 +58,12 @@ struct BwdArgs {
   void* dq_partial;      // FP32, or bf16 when bf16_partials
   void* dbias_partial;
   int B, N_o, H, N;
-  int n_key_tiles, n_groups;
+  int n_key_tiles;
+  // outer groups g0 .. g0 + n_groups - 1 run in this launch (all groups, or one chunk of
+  // the chunked backward); their dbias partials are planes 0 .. n_groups - 1 of
+  // dbias_partial, and the dQ partials hold part_slices slices per example (N_o, or
+  // n_groups * G), group g0 + i writing slices i * G ..
+  int g0, n_groups, part_slices;
   float scale;
   int bf16_partials;     // 1: partials stored as bf16 (one RNE rounding each)
 };
@@ -71,9 +76,30 @@ struct ReduceArgs {
   int bf16_partials;
 };
 
+// Segmented fixed-order sum of FP32 partials (the chunked backward's reductions).  Job j
+// covers nseg segments of seg_len elements; element i of segment s is
+//   x = (acc_in ? acc_in[s * seg_len + i] : first partial) + partials in ascending order,
+// partial p at partial[p * pstride + s * sstride + i].  The sum goes to acc_out (FP32, dense
+// [nseg, seg_len]) when acc_out is set, else rounded to bf16 into out[s * ostride + i].
+struct SegReduceJob {
+  const float* partial;
+  int64_t pstride, sstride, seg_len, ostride;
+  int n_partials, nseg;
+  const float* acc_in;
+  float* acc_out;
+  uint16_t* out;
+  int64_t blocks;        // workgroups of this job (set by the launcher)
+  int vec;               // every length and stride a multiple of 4 (set by the launcher)
+};
+struct SegReduceArgs {
+  SegReduceJob job[2];
+  int njobs;
+};
+
 hipError_t launch_fwd(const FwdArgs& a, int D, hipStream_t s);
 hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
+hipError_t launch_seg_reduce(SegReduceArgs a, hipStream_t s);
 
 }  // namespace tri
