@@ -183,6 +183,30 @@ tri_attn_status tri_attn_bwd_chunked(const tri_attn_dims* d,
                                      tri_attn_stream stream);
 
 /*
+ * Allocation-free variant of tri_attn_bwd_chunked, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments without the workspace: the chunk buffers live in a
+ * static device array of tri_attn_noalloc_scratch_bytes() bytes (128 MiB) that the
+ * library holds on every GPU it runs on until the process ends; its address is looked up
+ * once per device, on the first call on that device.  The call allocates and frees
+ * nothing.  Results are bitwise those of tri_attn_bwd_chunked (and of the unchunked
+ * calls).  Shapes for which not even one outer group's buffers fit in the scratch array
+ * (e.g. N = 4096, H = 4, where the FP32 running dbias sum alone is 256 MiB) return
+ * TRI_ATTN_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (concurrent streams, or host threads
+ * enqueueing at once) race on it and give undefined results; serialise them.  The array
+ * needs no clearing: each chunk writes every element it later reads.
+ */
+tri_attn_status tri_attn_bwd_chunked_noalloc(const tri_attn_dims* d,
+                                             const tri_bf16* q, const tri_bf16* k, const tri_bf16* v,
+                                             const tri_bf16* bias, const float* mask /* may be NULL */,
+                                             const tri_bf16* d_o, const float* lse, const float* delta,
+                                             tri_bf16* dq, tri_bf16* dk, tri_bf16* dv, tri_bf16* dbias,
+                                             tri_attn_stream stream);
+/* Size in bytes of the scratch array behind tri_attn_bwd_chunked_noalloc. */
+int64_t tri_attn_noalloc_scratch_bytes(void);
+
+/*
  * Partial-buffer sizes for these dimensions (elements, FP32), the number of
  * key tiles J_K and of outer groups L, and the key-tile / group sizes used
  * (key tile 128; group G = 4 for D = 32, 6 for D = 16 with N even and 4 with N

@@ -332,3 +332,28 @@ def test_chunked_workspace_sizes(lib, B, N_o, H, N, D):
             (up(4 * B * H * N * N) if chunks > 1 else 0)
         got = api.chunked_workspace(d, C)
         assert got == {"bytes": want, "groups_per_chunk": Cc}, (C, got, want)
+
+
+def test_noalloc_validation_before_any_device_access(lib):
+    """The allocation-free backward checks its arguments, and that one outer group's buffers fit
+    its scratch array, before it looks the array up on the device."""
+    names = ("q", "k", "v", "bias", "mask", "d_o", "lse", "delta", "dq", "dk", "dv", "dbias")
+
+    def call(d, **ptrs):
+        a = {n: P for n in names}
+        a["mask"] = None
+        a.update(ptrs)
+        return lib.tri_attn_bwd_chunked_noalloc(None if d is None else ctypes.byref(d), *[a[n] for n in names], None)
+
+    assert lib.tri_attn_noalloc_scratch_bytes() == 128 * 2 ** 20
+    assert call(None) == 1
+    assert call(_dims(), dq=None) == 1
+    assert call(_dims(), dbias=MIS) == 4
+    assert call(_dims(D=48)) == 3
+    # N = 4096, H = 4: the FP32 running dbias sum alone is 256 MiB, past the 128 MiB scratch
+    assert call(_dims(N_o=64, H=4, N=4096)) == 6
+    # one outer group at N = 1536, H = 4, D = 32 still fits (37.7 MB dQ + 37.7 MB dbias + 37.7 MB sum)
+    need = ctypes.c_int64()
+    assert lib.tri_attn_bwd_chunked_workspace(ctypes.byref(_dims(N_o=1536, H=4, N=1536)), 1, ctypes.byref(need),
+                                              None) == 0
+    assert need.value <= lib.tri_attn_noalloc_scratch_bytes()

@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     forward,
     tri_attn_bwd,
     tri_attn_bwd_chunked,
+    tri_attn_bwd_chunked_noalloc,
     tri_attn_bwd_delta,
     tri_attn_fwd,
     tri_attn_reduce_dbias,

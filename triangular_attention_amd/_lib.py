@@ -35,6 +35,8 @@ EXPORTS = (
     "tri_attn_reduce_dbias_bf16p",
     "tri_attn_bwd_chunked_workspace",
     "tri_attn_bwd_chunked",
+    "tri_attn_bwd_chunked_noalloc",
+    "tri_attn_noalloc_scratch_bytes",
     "tri_attn_workspace",
     "tri_attn_status_string",
     "tri_attn_version",
@@ -136,6 +138,7 @@ def load() -> ctypes.CDLL:
         "tri_attn_workspace": [dp, i64p, i64p, i64p, i64p, i64p, i64p],
         "tri_attn_bwd_chunked_workspace": [dp, ctypes.c_int64, i64p, i64p],
         "tri_attn_bwd_chunked": [dp] + [vp] * 13 + [ctypes.c_int64, vp],
+        "tri_attn_bwd_chunked_noalloc": [dp] + [vp] * 13,
     }
     bp = ctypes.POINTER(BlockDims)
     sig.update({
@@ -166,6 +169,8 @@ def load() -> ctypes.CDLL:
         f.restype = ctypes.c_int
     lib.tri_attn_status_string.argtypes = [ctypes.c_int]
     lib.tri_attn_status_string.restype = ctypes.c_char_p
+    lib.tri_attn_noalloc_scratch_bytes.argtypes = []
+    lib.tri_attn_noalloc_scratch_bytes.restype = ctypes.c_int64
     lib.tri_attn_version.argtypes = []
     lib.tri_attn_version.restype = ctypes.c_char_p
     _lib = lib

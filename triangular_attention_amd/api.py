@@ -174,6 +174,25 @@ def tri_attn_bwd_chunked(d, q, k, v, bias, mask, d_o, lse, delta, dq, dk, dv, db
                                         _ptr(dbias), _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
+def tri_attn_bwd_chunked_noalloc(d, q, k, v, bias, mask, d_o, lse, delta, dq, dk, dv, dbias, stream=None):
+    """The chunked backward with the library's static scratch array (no allocation by the call)."""
+    B, N_o, H, N, D = d.B, d.N_o, d.H, d.N, d.D
+    x = (B, N_o, H, N, D)
+    for n, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, n, torch.bfloat16, x)
+    for n, t in (("bias", bias), ("dbias", dbias)):
+        _need(t, n, torch.bfloat16, (B, H, N, N))
+    if mask is not None:
+        _need(mask, "mask", torch.float32, (B, N_o, N))
+    _need(lse, "lse", torch.float32, (B, N_o, H, N))
+    _need(delta, "delta", torch.float32, (B, N_o, H, N))
+    lib = _lib.load()
+    _lib.check("tri_attn_bwd_chunked_noalloc",
+               lib.tri_attn_bwd_chunked_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
+                                                _ptr(d_o), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+                                                _ptr(dbias), _stream(stream)))
+
+
 # --------------------------------------------------------------------------- composite calls
 
 

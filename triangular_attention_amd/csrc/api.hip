@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/tri_attn.h"
 #include "kernels.h"
@@ -257,6 +258,30 @@ tri_attn_status chunked_impl(const tri_attn_dims* d, const tri_bf16* q, const tr
   return TRI_ATTN_OK;
 }
 
+// Device memory of the allocation-free backward: one array per GPU, held by the loaded code
+// object until the process ends.  Host code never uses the array's name as an address (it is
+// a host-side stand-in); the device address comes from hipGetSymbolAddress, once per device.
+constexpr int64_t kScratchBytes = int64_t(128) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __attribute__((used)) __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device (looked up on the first call on that device).
+tri_attn_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TRI_ATTN_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TRI_ATTN_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TRI_ATTN_OK;
+}
+
 tri_attn_status reduce_impl(const tri_attn_dims* d, const void* partial, tri_bf16* out, bool dq,
                             int bf16_partials, tri_attn_stream stream) {
   tri_attn_status st = check_dims(d);
@@ -330,5 +355,27 @@ tri_attn_status tri_attn_bwd_chunked(const tri_attn_dims* d, const tri_bf16* q, 
   return chunked_impl(d, q, k, v, bias, mask, d_o, lse, delta, dq, dk, dv, dbias, workspace, workspace_bytes,
                       (hipStream_t)stream);
 }
+
+tri_attn_status tri_attn_bwd_chunked_noalloc(const tri_attn_dims* d, const tri_bf16* q, const tri_bf16* k,
+                                             const tri_bf16* v, const tri_bf16* bias, const float* mask,
+                                             const tri_bf16* d_o, const float* lse, const float* delta,
+                                             tri_bf16* dq, tri_bf16* dk, tri_bf16* dv, tri_bf16* dbias,
+                                             tri_attn_stream stream) {
+  // validate everything before the scratch lookup touches the device
+  tri_attn_status st = check_dims(d);
+  if (st != TRI_ATTN_OK) return st;
+  if (!dq || !dk || !dv || !dbias) return TRI_ATTN_ERR_NULL;
+  st = check_bwd_inputs(d, q, k, v, bias, mask, d_o, lse, delta);
+  if (st != TRI_ATTN_OK) return st;
+  if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dbias)) return TRI_ATTN_ERR_ALIGN;
+  if (chunk_plan(d, 1).bytes > kScratchBytes) return TRI_ATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != TRI_ATTN_OK) return st;
+  return chunked_impl(d, q, k, v, bias, mask, d_o, lse, delta, dq, dk, dv, dbias, ws, kScratchBytes,
+                      (hipStream_t)stream);
+}
+
+int64_t tri_attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 }  // extern "C"
