@@ -52,6 +52,12 @@ def parse():
                     help="write a markdown summary of a rocprofv3 --kernel-trace --stats output dir and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn FETCH_SIZE / WRITE_SIZE counter runs into per-launch bytes and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PASS_DIR",
+                    help="summarise rocprofv3 --pmc passes (SQ_* / GRBM_* counters) into per-kernel "
+                         "utilisation figures (--out: the markdown file; --counters: the JSON they go to)")
+    ap.add_argument("--counters", default=os.path.join(ROOT, "profiles", "counters.json"),
+                    help="per-kernel counter summary (MFMA busy fraction etc.), valid for the sources it was "
+                         "measured on")
     ap.add_argument("--command", default="", help="the command line that produced the profile (recorded)")
     ap.add_argument("--out", default="", help="output file of the summarize modes")
     return ap.parse_args()
@@ -138,6 +144,87 @@ def summarize_trace(d, command, out):
     print(txt)
 
 
+N_XCD, N_SIMD = 8, 1024      # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def summarize_counters(dirs, workload, command, out, counters_json):
+    """Per-kernel utilisation from rocprofv3 --pmc passes (each pass its own run).
+
+    Per dispatch the counters are summed over the whole GPU: GRBM_GUI_ACTIVE over the 8 XCDs (so
+    GRBM_GUI_ACTIVE / 8 is the kernel's duration in GPU cycles), SQ_VALU_MFMA_BUSY_CYCLES and
+    SQ_VALU_MFMA_COEXEC_CYCLES over the 1024 SIMDs (cycles), SQ_ACTIVE_INST_VALU over waves (issue
+    cycles of 4 clocks each for wave64).  Fractions are of the SIMD cycles of the dispatch:
+    MFMA busy = MFMA_BUSY / (1024 * cycles); VALU busy = 4 * ACTIVE_INST_VALU / (1024 * cycles);
+    co-exec = COEXEC / (1024 * cycles).  The median over dispatches is taken per counter."""
+    import csv
+    import glob
+    vals = {}
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            for r in csv.DictReader(open(f)):
+                k = _short_kernel_name(r["Kernel_Name"])
+                if k.startswith("copy:"):
+                    continue
+                dur = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-3
+                v = vals.setdefault(k, {})
+                v.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                v.setdefault("_dur_us", []).append(dur)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    res = {"workload": workload, "kernel_hash": kernel_hash(_hash_files(workload)), "command": command,
+           "kernels": {}}
+    for k, v in vals.items():
+        m = {c: med(x) for c, x in v.items()}
+        g = m.get("GRBM_GUI_ACTIVE")
+        if not g:
+            continue
+        cyc = g / N_XCD
+        row = {"cycles": cyc, "us_under_counters": m["_dur_us"],
+               "clock_ghz": cyc / (m["_dur_us"] * 1e3) if m["_dur_us"] > 0 else None}
+        simd = N_SIMD * cyc
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            row["mfma_busy"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / simd
+        if "SQ_ACTIVE_INST_VALU" in m:
+            row["valu_busy"] = 4.0 * m["SQ_ACTIVE_INST_VALU"] / simd
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
+            row["mfma_valu_coexec"] = m["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd
+        if "SQ_INSTS_MFMA" in m and m["SQ_INSTS_MFMA"] > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            row["mfma_cycles_per_inst"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / m["SQ_INSTS_MFMA"]
+        waves = m.get("SQ_WAVES")
+        for c, name in (("SQ_INSTS_VALU", "valu_insts_per_wave"), ("SQ_INSTS_MFMA", "mfma_insts_per_wave"),
+                        ("SQ_INSTS_LDS", "lds_insts_per_wave"), ("SQ_INSTS_SALU", "salu_insts_per_wave"),
+                        ("SQ_INSTS_VMEM_RD", "vmem_rd_insts_per_wave")):
+            if waves and c in m:
+                row[name] = m[c] / waves
+        if "SQ_WAIT_INST_ANY" in m and "SQ_WAVE_CYCLES" in m and m["SQ_WAVE_CYCLES"] > 0:
+            row["wave_wait_inst_frac"] = m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"]
+        if "SQ_LDS_BANK_CONFLICT" in m and "SQ_ACTIVE_INST_LDS" in m and m["SQ_ACTIVE_INST_LDS"] > 0:
+            row["lds_bank_conflict_per_lds_inst"] = m["SQ_LDS_BANK_CONFLICT"] / m["SQ_ACTIVE_INST_LDS"]
+        row["raw_median"] = {c: x for c, x in m.items() if not c.startswith("_")}
+        res["kernels"][k] = row
+    old = json.load(open(counters_json)) if os.path.exists(counters_json) else {}
+    old[workload] = res
+    open(counters_json, "w").write(json.dumps(old, indent=1) + "\n")
+    f = lambda x, p=1: "-" if x is None else (f"{100 * x:.{p}f}%")
+    lines = ["# rocprofv3 counter summary: " + workload, "",
+             f"Command: `{command}`", "",
+             "Fractions are of the SIMD cycles of each dispatch (1024 SIMDs x GRBM_GUI_ACTIVE / 8 cycles); "
+             "median over dispatches.  Kernel sources hash: " + res["kernel_hash"] + ".", "",
+             "| kernel | cycles | clock (GHz) | MFMA busy | VALU busy | MFMA+VALU co-exec | MFMA cycles/inst | "
+             "VALU inst/wave | MFMA inst/wave | LDS inst/wave | wait-inst share | LDS conflicts/LDS inst |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k, r in res["kernels"].items():
+        g = lambda n, fmt="{:.1f}": "-" if r.get(n) is None else fmt.format(r[n])
+        lines.append(f"| {k} | {r['cycles']:.3g} | {g('clock_ghz', '{:.2f}')} | {f(r.get('mfma_busy'))} | "
+                     f"{f(r.get('valu_busy'))} | {f(r.get('mfma_valu_coexec'))} | {g('mfma_cycles_per_inst')} | "
+                     f"{g('valu_insts_per_wave', '{:.0f}')} | {g('mfma_insts_per_wave', '{:.0f}')} | "
+                     f"{g('lds_insts_per_wave', '{:.0f}')} | {f(r.get('wave_wait_inst_frac'))} | "
+                     f"{g('lds_bank_conflict_per_lds_inst', '{:.2f}')} |")
+    txt = "\n".join(lines) + "\n"
+    if out:
+        open(out, "w").write(txt)
+    print(txt)
+
+
 def summarize_pmc(fetch_dir, write_dir, workload, copy_bytes, command, out):
     """Per-launch HBM bytes of every kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for the plain copy of copy_bytes bytes."""
@@ -183,6 +270,9 @@ def main():
     args = parse()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.command, args.out)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload, args.command, args.out, args.counters)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.copy_bytes,
@@ -322,6 +412,10 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach_b, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach_b / PEAK_HBM_GBS, 4), **common}
 
+    # measured utilisation of the dominant kernel (rocprofv3 counters taken on these sources)
+    cnt = _counters_lookup(args.counters, w.name, dom + "_kernel")
+    if cnt is not None:
+        roof["counters"] = cnt
     value = w.flops_fwd_bwd / (ms_step * 1e-3) / 1e12
     out = {
         "metric": "tri-attn fwd+bwd TFLOP/s & ms at N=768,H=4,D=32 bf16; % bf16 MFMA peak",
@@ -430,6 +524,24 @@ def _traffic_lookup(path, workload, dom, prefix):
         return None, allk
     except Exception:
         return None, None
+
+
+def _counters_lookup(path, workload, prefix):
+    """MFMA / VALU busy fractions of a kernel from the counter summary, if it was taken on the
+    current sources."""
+    if not os.path.exists(path):
+        return None
+    try:
+        c = json.load(open(path)).get(workload, {})
+        if c.get("kernel_hash") != kernel_hash(_hash_files(workload)):
+            return None
+        for k, v in c["kernels"].items():
+            if k.startswith(prefix):
+                return {"kernel": k, **{n: round(v[n], 4) for n in ("mfma_busy", "valu_busy", "mfma_valu_coexec",
+                                                                     "clock_ghz") if v.get(n) is not None}}
+    except Exception:
+        return None
+    return None
 
 
 def _copy_calibration(args, dev, out):
