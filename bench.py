@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--chunk-groups", type=int, default=0,
                     help="run the backward as tri_attn_bwd_chunked with chunks of this many outer groups "
                          "(bounded partial memory); 0 = the unchunked calls")
+    ap.add_argument("--sweep", action="store_true",
+                    help="bench the pages' six timing shapes and the three configured workloads, each with the "
+                         "oracle timed beside it (--cpu-seconds each), and print a table")
     ap.add_argument("--cpu-seconds", type=float, default=25.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -300,7 +303,54 @@ def main():
     if args.workload in synth.TRIMUL_WORKLOADS:
         bench_trimul(args, synth.TRIMUL_WORKLOADS[args.workload], dev)
         return
-    w = synth.get(args.workload)
+    if args.sweep:
+        sweep(args, dev)
+        return
+    out = bench_attn(args, synth.get(args.workload), dev)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(synth.get(args.workload), args.cpu_seconds)
+    print(json.dumps(out))
+
+
+# the three configured workloads (n384_d32 is also the sweep's 384 x 32 shape) and the rest of the
+# pages' six timing shapes
+SWEEP_WORKLOADS = ("n384_d32", "n640_d16", "n768_d32_mask", "sweep_n384_d16", "sweep_n640_d16", "sweep_n640_d32",
+                   "sweep_n768_d16", "sweep_n768_d32")
+
+
+def sweep(args, dev):
+    """The pages' six timing shapes (crops 384/640/768 x D 16/32) and the three configured workloads:
+    one bench line each (ms, TFLOP/s, the dominant kernel's roofline fraction) with the FP64
+    oracle timed on a short sample of the same workload beside it, then a markdown table."""
+    import synth
+    rows = []
+    for name in SWEEP_WORKLOADS:
+        w = synth.get(name)
+        out = bench_attn(args, w, dev)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        print(json.dumps(out), flush=True)
+        rows.append(out)
+    print("| workload | ms / fwd+bwd | TFLOP/s | % bf16 peak | fwd ms | bwd ms (delta + main + reductions) | "
+          "dominant kernel | its bound | its roofline fraction | oracle TFLOP/s (cores) | GPU / oracle |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        k = r["kernels"]
+        bwd = sum(v["ms"] for n, v in k.items() if n != "fwd")
+        cb = r.get("cpu_baseline")
+        ro = r["roofline"]
+        print(f"| {r['config']['workload']} | {r['ms_per_step']:.3f} | {r['value']:.0f} | {r['pct_bf16_peak']:.1f} | "
+              f"{k['fwd']['ms']:.3f} | {bwd:.3f} | {ro['kernel']} | {ro['bound']} | {ro['frac']:.3f} | "
+              + (f"{cb['value']:.3f} ({cb['cores']}) | {r['value'] / cb['value']:.0f}x |" if cb else "- | - |"))
+
+
+def bench_attn(args, w, dev):
+    """One bench line (dict) for an attention workload: the five calls (or the chunked
+    backward) timed on resident inputs, per-kernel times and the dominant kernel's roofline."""
+    import torch
+
+    import synth
+    import triangular_attention_amd as ta
     x = synth.make_inputs(w, args.seed)
     q, k, v, do, bias = (x[n].to(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do", "bias"))
     mask = None if x["mask"] is None else x["mask"].to(dev)
@@ -445,17 +495,8 @@ def main():
     }
     if traffic_all is not None:
         out["traffic_bytes_per_launch"] = {k: round(v["bytes_per_launch"]) for k, v in traffic_all.items()}
-    if args.copy_bytes > 0:
-        n = args.copy_bytes // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        out["copy_calibration_bytes"] = args.copy_bytes
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(out))
+    _copy_calibration(args, dev, out)
+    return out
 
 
 BLOCK_KERNELS = ("ln_proj", "fwd", "gate_out", "gate_out_bwd", "delta", "bwd", "reduce_dbias", "reduce_dq",
