@@ -218,7 +218,7 @@ tri_attn_status tri_attn_workspace(const tri_attn_dims* d, int64_t* dq_partial_e
                                    int64_t* key_tile, int64_t* outer_group);
 
 /* Human-readable name of a status code (static string). */
-const char* tri_attn_status_string(tri_attn_status s);
+const char* tri_attn_status_string(int status);   /* any int; unknown codes -> "unknown status" */
 
 /* Library version, e.g. "0.1.0". */
 const char* tri_attn_version(void);

@@ -11,7 +11,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtri_attn.so")
+# TRI_ATTN_LIBRARY points the binding at another build of the same sources (the host-sanitizer
+# build of the CPU checks); by default the in-tree library
+LIB_PATH = os.environ.get("TRI_ATTN_LIBRARY") or os.path.join(HERE, "libtri_attn.so")
 
 STATUS = {
     0: "TRI_ATTN_OK",

@@ -44,8 +44,9 @@ tri_attn_status launched(hipError_t e) { return e == hipSuccess ? TRI_ATTN_OK : 
 
 extern "C" {
 
-const char* tri_attn_status_string(tri_attn_status s) {
-  switch (s) {
+const char* tri_attn_status_string(int status) {
+  // an int, not the enum: any code a caller passes is a defined value here
+  switch (status) {
     case TRI_ATTN_OK: return "ok";
     case TRI_ATTN_ERR_NULL: return "null pointer argument";
     case TRI_ATTN_ERR_SHAPE: return "invalid dimensions or scale";
