@@ -102,10 +102,25 @@ __device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds
 // wait-count bookkeeping.  The compiler tracks every direct load it knows of as a
 // pending LDS write and waits for it (vmcnt(0)) before any LDS read it cannot prove
 // disjoint, which would serialise a prefetch into one buffer with the reads of the
-// other.  Callers of this form wait for their direct loads themselves (s_waitcnt
-// vmcnt(0) before the barrier that publishes a tile).  The compiler's own counted
-// waits stay correct: a load it tracks cannot complete before the younger loads it
-// also tracks, so untracked loads only make those waits stricter.
+// other.  The compiler's own counted waits stay correct: a load it tracks cannot
+// complete before the younger loads it also tracks, so untracked loads only make
+// those waits stricter.
+//
+// Wait invariant that every caller of dma16 / dma4 keeps (the compiler cannot):
+//  1. a wave's direct loads have landed in LDS only after that wave has executed
+//     s_waitcnt vmcnt(0): they do not complete in order with register loads, so a
+//     counted wait vmcnt(n > 0) is never used to cover them;
+//  2. other waves may read the data only after the loading wave's vmcnt(0) is
+//     followed by a workgroup barrier (lds_barrier) that the readers also pass;
+//  3. a buffer is refilled only after a barrier that every wave reading its previous
+//     contents passed after its last read of them (lds_barrier waits lgkmcnt(0), so
+//     those reads have returned).
+// Forward: each wave issues the loads of tile kt + 2 right after the barrier that
+// ends tile kt (into the buffer tile kt used) and waits vmcnt(0) just before the
+// barrier that ends tile kt + 1.  Backward: loader set s % 2 issues stage s right
+// after the barrier that ends stage s - 3 (into the buffer stage s - 3 used) and
+// waits vmcnt(0) just before the barrier that ends stage s - 1; the other set's
+// loads stay in flight across that barrier and are waited for a stage later.
 // rsrc: buffer descriptor words (wave-uniform); lds: wave-uniform LDS address (M0).
 __device__ __forceinline__ u32x4 make_rsrc_words(const void* base, uint32_t bytes) {
   const uint64_t b = (uint64_t)base;
@@ -190,8 +205,8 @@ __device__ __forceinline__ u32x4 ds_read_tr8_at(const uint16_t* tile, int off_lo
 // Workgroup barrier for LDS tiles filled by direct global->LDS loads.
 // __syncthreads() also orders global memory, which makes the compiler wait for
 // every outstanding vector-memory load (register prefetches included) before
-// the barrier.  Here the caller waits for the direct loads explicitly (in-order
-// completion, s_waitcnt vmcnt(n)), this wave's LDS reads are waited for
+// the barrier.  Here the caller waits for its direct loads explicitly (vmcnt(0),
+// see the wait invariant above), this wave's LDS reads are waited for
 // (lgkmcnt(0)), and compiler barriers keep memory accesses on their side.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), other counters unconstrained
