@@ -422,30 +422,45 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     }
   };
 
-  // ---- dQ^T block (queries 16qb.., features 16db..) = K^T dS^T over the TK keys of a stage;
-  // wave w computes block w.  The partial's descriptor starts at the tile's first row and
-  // ends at row N (extent zero when nothing is to be stored), so rows past N are dropped.
-  auto dq_stage = [&](int jj, int gg, int buf, bool store) {
-    if (w < NBLK) {
-      const int qb = w / NDB, db = w % NDB;
-      const uint16_t* kt_tile = sK[gg];
+  // ---- dQ^T blocks (queries 16qb.., features 16db..) = K^T dS^T over the TK keys of a stage.
+  // Each partial's descriptor starts at the tile's first row and ends at row N (extent zero
+  // when nothing is to be stored), so rows past N are dropped.
+  // Who computes them: on the direct path, the loader set that does not wait at the end of
+  // the stage (wave ws of the set takes the DQB blocks of one query block starting at
+  // feature block ws * DQB % NDB); its partial stores then have two stages to drain before
+  // that set's next vmcnt(0), which on this hardware also waits for the wave's stores
+  // (measured at N = 768: 1.63 -> 1.53 ms for D = 32, 1.18 -> 1.13 ms for D = 16, 3.50 ->
+  // 3.46 ms for D = 64).  On the register path wave w takes block w.
+  constexpr bool DSET = VEC;
+  constexpr int DQB = DSET ? NBLK / HW : 1;     // dQ blocks per computing wave
+  static_assert(!DSET || (NBLK % HW == 0 && NDB % DQB == 0), "a wave's dQ blocks share one query block");
+  auto dq_blocks = [&](int jj, int gg, int buf, bool store, int blk0) {
+    const int qb = blk0 / NDB;
+    const uint16_t* kt_tile = sK[gg];
+    // the dS^T operand of the query block, shared by the wave's feature blocks
+    u32x4 bs[TK / 32];
+#pragma unroll
+    for (int st = 0; st < TK / 32; ++st) {
+      const int so = (32 * st + 8 * g + trk) * SP + 16 * qb + 4 * tra;
+      bs[st] = ds_read_tr8_at(sdS[buf], so, so + 4 * SP);
+    }
+    const int64_t prow = t * part_rows + prow0 + (gg < nsl ? gg : 0) * ostride + (int64_t)jj * TQ;
+#pragma unroll
+    for (int bb = 0; bb < DQB; ++bb) {
+      const int db = (blk0 + bb) % NDB;
       f32x4 dq0 = f32x4{0.f, 0.f, 0.f, 0.f}, dq1 = f32x4{0.f, 0.f, 0.f, 0.f};
-      // all operand reads first, so their LDS latency overlaps
-      u32x4 ak[TK / 32], bs[TK / 32];
+      u32x4 ak[TK / 32];
 #pragma unroll
       for (int st = 0; st < TK / 32; ++st) {
         const int kr = 32 * st + 8 * g + trk;
         const int kc = 16 * db + 4 * tra;
         ak[st] = ds_read_tr8_at(kt_tile, Lay<D>::k(kr, kc), Lay<D>::k(kr + 4, kc));
-        const int so = (32 * st + 8 * g + trk) * SP + 16 * qb + 4 * tra;
-        bs[st] = ds_read_tr8_at(sdS[buf], so, so + 4 * SP);
       }
 #pragma unroll
       for (int st = 0; st < TK / 32; ++st) {
         if (st & 1) dq1 = mfma_k32(ak[st], bs[st], dq1);
         else dq0 = mfma_k32(ak[st], bs[st], dq0);
       }
-      const int64_t prow = t * part_rows + prow0 + (gg < nsl ? gg : 0) * ostride + (int64_t)jj * TQ;
       const f32x4 v = (dq0 + dq1) * scale;
       if constexpr (BP) {   // bf16 partials: one RNE rounding, 8 bytes per lane
         const uint32_t ext = __builtin_amdgcn_readfirstlane(store && gg < nsl ? (uint32_t)(N - jj * TQ) * D * 2 : 0u);
@@ -458,6 +473,14 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         const uint32_t off = (uint32_t)((16 * qb + c) * D + 16 * db + 4 * g) * 4;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
       }
+    }
+  };
+  // dset: the loader set that does not wait at the end of the current stage
+  auto dq_stage = [&](int jj, int gg, int buf, bool store, int dset) {
+    if constexpr (DSET) {
+      if (lset == dset) dq_blocks(jj, gg, buf, store, ws * DQB);
+    } else {
+      if (w < NBLK) dq_blocks(jj, gg, buf, store, w);
     }
   };
 
@@ -516,8 +539,9 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       // dQ of the previous stage, (j, gs-1) or (j-1, G-1), whose dS^T tile was completed
       // at the previous barrier; before the first stage it runs on the idle buffer and
       // stores nothing
-      if (gs > 0) dq_stage(j, gs - 1, dsb ^ 1, true);
-      else dq_stage(j > 0 ? j - 1 : 0, G - 1, dsb ^ 1, j > 0);
+      // (the set waiting at the end of stage r is (r + 1) & 1, see below)
+      if (gs > 0) dq_stage(j, gs - 1, dsb ^ 1, true, r & 1);
+      else dq_stage(j > 0 ? j - 1 : 0, G - 1, dsb ^ 1, j > 0, r & 1);
 
       const auto lk = [](int r, int cc) { return Lay<D>::k(r, cc); };
       const auto lv = [](int r, int cc) { return Lay<D>::v(r, cc); };
@@ -646,7 +670,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   };
   if (nsl == G) run(std::true_type{});
   else run(std::false_type{});
-  dq_stage(nqt - 1, G - 1, (G - 1) & 1, true);
+  dq_stage(nqt - 1, G - 1, (G - 1) & 1, true, 0);
 
   // epilogue: dK = scale * dK^T^T, dV
   if (kok) {
