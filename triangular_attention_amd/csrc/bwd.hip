@@ -432,6 +432,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   // (measured at N = 768: 1.63 -> 1.53 ms for D = 32, 1.18 -> 1.13 ms for D = 16, 3.50 ->
   // 3.46 ms for D = 64).  On the register path wave w takes block w.
   constexpr bool DSET = VEC;
+  constexpr bool DEARLY = VEC && D == 64;   // dbias stores split around the last stage's barrier
   constexpr int DQB = DSET ? NBLK / HW : 1;     // dQ blocks per computing wave
   static_assert(!DSET || (NBLK % HW == 0 && NDB % DQB == 0), "a wave's dQ blocks share one query block");
   auto dq_blocks = [&](int jj, int gg, int buf, bool store, int blk0) {
@@ -526,6 +527,40 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       bb[qb] = f32x4{bf_lo(bw[0]), bf_hi(bw[0]), bf_lo(bw[1]), bf_hi(bw[1])} * kLog2e;
     }
     f32x4 dbacc[NQB];       // sum over the group's slices of the FP32 dS, in slice order
+    // this group's dbias partial of query tile j (the FP32 sum over the group's slices)
+    auto store_dbias = [&]() {
+      if (kok) {
+        // this group's dbias partial for (query tile j, key tile t); in the last query
+        // tile rows past N go to an offset past the plane's extent and are dropped
+        const int64_t plane = (((int64_t)grp_l * a.B + b) * H + h) * N * N;
+        constexpr int EB = BP ? 2 : 4;         // bytes per partial element
+        const __amdgpu_buffer_rsrc_t rs =
+            BP ? make_rsrc((uint16_t*)a.dbias_partial + plane, (uint32_t)N * N * 2)
+               : make_rsrc((float*)a.dbias_partial + plane, (uint32_t)N * N * 4);
+        auto put = [&](float x, uint32_t voff, int soff) {
+          if constexpr (BP) __builtin_amdgcn_raw_buffer_store_b16(f_to_bf(x), rs, voff, soff, 0);
+          else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, voff, soff, 0);
+        };
+        if ((j + 1) * TQ <= N) {
+          const uint32_t lane_off = (uint32_t)(8 * g * N + key) * EB;
+  #pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int rr = j * TQ + 32 * (qb >> 1) + 4 * (qb & 1) + i;   // row of group g = 0
+              put(dbacc[qb][i], lane_off, (int)((uint32_t)rr * N * EB));
+            }
+        } else {
+  #pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int q = j * TQ + 32 * (qb >> 1) + 8 * g + 4 * (qb & 1) + i;
+              put(dbacc[qb][i], q < N ? (uint32_t)(q * N + key) * EB : 0xFFFFF000u, 0);
+            }
+        }
+      }
+    };
 
 #pragma unroll
     for (int gs = 0; gs < G; ++gs) {
@@ -593,6 +628,13 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         }
       }
 
+      // the dbias partial: with D = 64 (two slices per group, 32-query stages) the set that
+      // does not wait at the end of the tile's last stage stores it before that stage's
+      // barrier, so its stores drain during the rest of this stage and all of the next before
+      // that set's own vmcnt(0); the other set stores it after the barrier, two stages before
+      // its wait (measured at N = 768: 3.44 -> 2.96 ms; no gain for D = 16 and 32, where a
+      // tile has four stages, so the stores stay after the barrier there)
+      if (DEARLY && gs == G - 1 && lset == (r & 1)) store_dbias();
       if (VEC) {
         // the set that loaded stage s+1 waits for it and stages its -lse/-delta; the
         // other set's loads (stage s+2) stay in flight across this barrier
@@ -621,38 +663,8 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         if (gs == G - 1 && j + 2 < nqt) load_bias_regs(j + 2);
       }
     }
+    if (!DEARLY || lset != ((R0 + G - 1) & 1)) store_dbias();
 
-    if (kok) {
-      // this group's dbias partial for (query tile j, key tile t); in the last query
-      // tile rows past N go to an offset past the plane's extent and are dropped
-      const int64_t plane = (((int64_t)grp_l * a.B + b) * H + h) * N * N;
-      constexpr int EB = BP ? 2 : 4;         // bytes per partial element
-      const __amdgpu_buffer_rsrc_t rs =
-          BP ? make_rsrc((uint16_t*)a.dbias_partial + plane, (uint32_t)N * N * 2)
-             : make_rsrc((float*)a.dbias_partial + plane, (uint32_t)N * N * 4);
-      auto put = [&](float x, uint32_t voff, int soff) {
-        if constexpr (BP) __builtin_amdgcn_raw_buffer_store_b16(f_to_bf(x), rs, voff, soff, 0);
-        else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, voff, soff, 0);
-      };
-      if ((j + 1) * TQ <= N) {
-        const uint32_t lane_off = (uint32_t)(8 * g * N + key) * EB;
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int rr = j * TQ + 32 * (qb >> 1) + 4 * (qb & 1) + i;   // row of group g = 0
-            put(dbacc[qb][i], lane_off, (int)((uint32_t)rr * N * EB));
-          }
-      } else {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int q = j * TQ + 32 * (qb >> 1) + 8 * g + 4 * (qb & 1) + i;
-            put(dbacc[qb][i], q < N ? (uint32_t)(q * N + key) * EB : 0xFFFFF000u, 0);
-          }
-      }
-    }
   };
   using R0a = std::integral_constant<int, 0>;
   using R0b = std::integral_constant<int, G>;
