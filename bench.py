@@ -66,9 +66,11 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic(w, jk, L, pb=4):
-    """Algorithmic flops and minimum HBM bytes of one launch of each kernel (pb = bytes per
-    partial element)."""
+def algorithmic(w, jk, L, pb=4, two_kernel=False):
+    """Algorithmic flops and minimum HBM bytes of one launch of each call (pb = bytes per
+    partial element).  The backward call's flops are the method's (one recompute of S); its
+    bytes are each tensor once per kernel: with two kernels (dK/dV key-tile kernel and dQ/dbias
+    query-tile kernel) Q, K, V, dO, the bias, lse, delta and the mask are read by both."""
     X = w.B * w.N_o * w.H * w.N * w.D
     Y = w.B * w.H * w.N * w.N
     R = w.B * w.N_o * w.H * w.N
@@ -78,7 +80,8 @@ def algorithmic(w, jk, L, pb=4):
         "fwd": {"flops": 4.0 * S * w.D, "bytes": 2 * (3 * X + Y + 2 * X) + 4 * (M + R)},
         "delta": {"flops": 2.0 * X, "bytes": 2 * 3 * X + 4 * R},
         "bwd": {"flops": 10.0 * S * w.D,
-                "bytes": 2 * (4 * X + Y + 2 * X) + 4 * (2 * R + M) + pb * (jk * X + L * Y)},
+                "bytes": (2 * (8 * X + 2 * Y + 2 * X) + 4 * (4 * R + 2 * M) if two_kernel else
+                          2 * (4 * X + Y + 2 * X) + 4 * (2 * R + M)) + pb * (jk * X + L * Y)},
         "reduce_dq": {"flops": float(jk * X), "bytes": pb * jk * X + 2 * X},
         "reduce_dbias": {"flops": float(L * Y), "bytes": pb * L * Y + 2 * Y},
     }
@@ -355,7 +358,10 @@ def bench_attn(args, w, dev):
     q, k, v, do, bias = (x[n].to(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do", "bias"))
     mask = None if x["mask"] is None else x["mask"].to(dev)
     d = ta.dims_of(q, w.scale)
-    ws = ta.workspace(d)
+    bp = args.partials == "bf16"
+    ws = ta.workspace(d, single_pass=bp)
+    # the default FP32 backward call runs two kernels for D = 32 (dK/dV, then dQ/dbias)
+    two = w.D == 32 and not bp
     comp = not args.no_compensate
     o = torch.empty_like(q)
     o_res = torch.empty_like(q) if comp else None
@@ -363,7 +369,6 @@ def bench_attn(args, w, dev):
     delta = torch.empty_like(lse)
     dk, dv, dq = torch.empty_like(k), torch.empty_like(v), torch.empty_like(q)
     dbias = torch.empty_like(bias)
-    bp = args.partials == "bf16"
     pdt = torch.bfloat16 if bp else torch.float32
     dqp = torch.empty(ws["dq_partial_elems"], dtype=pdt, device=dev)
     dbp = torch.empty(ws["dbias_partial_elems"], dtype=pdt, device=dev)
@@ -423,7 +428,7 @@ def bench_attn(args, w, dev):
         for i, n in enumerate(names):
             per[n] += evs[s][i].elapsed_time(evs[s][i + 1]) / args.steps
 
-    alg = algorithmic(w, ws["j_k"], ws["l"], 2 if bp else 4)
+    alg = algorithmic(w, ws["j_k"], ws["l"], 2 if bp else 4, two_kernel=two)
     # the chunked call does the work of the main backward and both reductions
     alg["bwd_chunked"] = {k: alg["bwd"][k] + alg["reduce_dq"][k] + alg["reduce_dbias"][k] for k in ("flops", "bytes")}
     kernels = {}
@@ -433,6 +438,8 @@ def bench_attn(args, w, dev):
                       "tflops": round(alg[n]["flops"] / (ms * 1e-3) / 1e12, 2) if ms > 0 else None,
                       "alg_gbs": round(alg[n]["bytes"] / (ms * 1e-3) / 1e9, 1) if ms > 0 else None}
     dom = max(names, key=lambda n: per[n])
+    # kernels of the dominant call (the two-kernel backward call launches both)
+    prefixes = (dom + "_kernel",) + (("bwdq_kernel",) if dom == "bwd" and two else ())
     traffic = None
     traffic_all = None
     if os.path.exists(args.traffic):
@@ -440,9 +447,9 @@ def bench_attn(args, w, dev):
             tr = json.load(open(args.traffic)).get(w.name, {})
             if tr.get("kernel_hash") == kernel_hash():
                 traffic_all = tr["kernels"]
-                for kname, v in traffic_all.items():
-                    if kname.startswith(dom + "_kernel"):
-                        traffic = round(v["bytes_per_launch"])
+                hits = [v["bytes_per_launch"] for kname, v in traffic_all.items() if kname.startswith(prefixes)]
+                if len(hits) == len(prefixes):
+                    traffic = round(sum(hits))
         except Exception:
             traffic = None
     # roofline of the dominant kernel: the bound is the resource whose peak gives the longer
@@ -452,7 +459,8 @@ def bench_attn(args, w, dev):
     t_hbm = alg[dom]["bytes"] / (PEAK_HBM_GBS * 1e9)
     ach_f = alg[dom]["flops"] / (per[dom] * 1e-3) / 1e12
     ach_b = alg[dom]["bytes"] / (per[dom] * 1e-3) / 1e9
-    common = {"kernel": dom, "traffic": traffic, "avg_launch_ms": round(per[dom], 5),
+    common = {"kernel": dom + (" (two kernels: dK/dV key-tile, dQ/dbias query-tile)" if dom == "bwd" and two else ""),
+              "traffic": traffic, "avg_launch_ms": round(per[dom], 5),
               "intensity_flop_per_byte": round(alg[dom]["flops"] / alg[dom]["bytes"], 1),
               "mfma_frac": round(ach_f / PEAK_BF16_TFLOPS, 4), "hbm_frac": round(ach_b / PEAK_HBM_GBS, 4)}
     if t_mfma >= t_hbm:
@@ -463,9 +471,9 @@ def bench_attn(args, w, dev):
                 "unit": "GB/s", "frac": round(ach_b / PEAK_HBM_GBS, 4), **common}
 
     # measured utilisation of the dominant kernel (rocprofv3 counters taken on these sources)
-    cnt = _counters_lookup(args.counters, w.name, dom + "_kernel")
-    if cnt is not None:
-        roof["counters"] = cnt
+    cnt = [c for c in (_counters_lookup(args.counters, w.name, p) for p in prefixes) if c is not None]
+    if cnt:
+        roof["counters"] = cnt[0] if len(cnt) == 1 else cnt
     value = w.flops_fwd_bwd / (ms_step * 1e-3) / 1e12
     out = {
         "metric": "tri-attn fwd+bwd TFLOP/s & ms at N=768,H=4,D=32 bf16; % bf16 MFMA peak",
@@ -882,7 +890,8 @@ def _hash_files(workload):
     return None if workload.startswith(("block", "trimul")) else ATTN_SOURCES
 
 
-ATTN_SOURCES = ("common.h", "kernels.h", "api.hip", "fwd.hip", "bwd.hip", "delta_reduce.hip")
+ATTN_SOURCES = ("common.h", "kernels.h", "bwd_layout.h", "api.hip", "fwd.hip", "bwd.hip", "bwd_q.hip",
+                "delta_reduce.hip")
 BLOCK_SOURCES = ("common.h", "block_kernels.h", "block_api.hip", "block.hip")
 
 

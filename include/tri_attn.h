@@ -23,7 +23,7 @@
  *   dq_partial                     [J_K, B, N_o, H, N, D] fp32
  *   dbias_partial                  [L,   B, H, N, N]      fp32
  * with J_K = ceil(N / key tile) and L = ceil(N_o / outer group) as reported by
- * tri_attn_workspace().
+ * tri_attn_workspace() (the bf16-partial calls: tri_attn_workspace_single_pass()).
  *
  * Ownership: every pointer is a DEVICE pointer owned by the caller.  The
  * library allocates nothing, frees nothing and never synchronises; each call
@@ -104,12 +104,21 @@ tri_attn_status tri_attn_bwd_delta(const tri_attn_dims* d, const tri_bf16* o,
                                    tri_attn_stream stream);
 
 /*
- * Main key-tile backward (Figure 2, Figure 7(c)).  One workgroup owns one key
- * tile of one head for one outer group of slices and visits every query tile,
- * evaluating S, P, dP and dS once.  dK and dV (scaled by `scale` for dK) are
- * finished in the workgroup; dQ (already scaled) leaves as one FP32 partial per
- * key tile and dbias as one FP32 partial per outer group, each element written
- * by exactly one workgroup (Figure 11(a), materialised partials).
+ * Main backward (Figure 2).  dK and dV (scaled by `scale` for dK) are finished here;
+ * dQ (already scaled) leaves as J_K FP32 partials and dbias as L FP32 partials, each
+ * element written by exactly one workgroup (Figure 11(a), materialised partials), with
+ * J_K and L as reported by tri_attn_workspace.
+ *   D = 16, 64: the single-pass key-tile kernel (Figure 7(c)): one workgroup owns one
+ *     128-key tile of one head for one outer group of G slices and visits every query
+ *     tile, evaluating S, P, dP and dS once; one dQ partial per key tile, one dbias
+ *     partial per outer group.
+ *   D = 32: two kernels.  The key-tile kernel forms dK and dV only; a query-tile kernel
+ *     then evaluates S, P, dP and dS again per (32 queries, range of up to 768 keys,
+ *     outer group of up to N_o / L slices), sums each slice's dQ over the key range and
+ *     the dbias of its (query, key) block over the whole outer group inside the workgroup:
+ *     J_K = ceil(N / 768) dQ partials and L <= 64 dbias partials (L = 8 at N = 768), a
+ *     small fraction of the single-pass kernel's partial bytes.
+ * Either way every sum has a fixed order, so results are bitwise reproducible.
  */
 tri_attn_status tri_attn_bwd(const tri_attn_dims* d,
                              const tri_bf16* q, const tri_bf16* k, const tri_bf16* v,
@@ -128,13 +137,14 @@ tri_attn_status tri_attn_reduce_dbias(const tri_attn_dims* d, const float* dbias
                                       tri_bf16* dbias, tri_attn_stream stream);
 
 /*
- * BF16-partial variant (the pages size the partials in BF16, Table 2): the same
- * three calls with the dQ and dbias partials stored as bf16 — each partial element
- * is the FP32 value rounded once to bf16 (round to nearest even) before it is
- * stored; the reductions add the partials in FP32 in the same fixed order.  Half
- * the partial bytes, at the cost of one bf16 rounding per partial.  Buffers hold
- * the element counts of tri_attn_workspace, 2 bytes each, 16-byte aligned.  The
- * FP32 calls above remain the reference path.  Errors as for those calls.
+ * BF16-partial variant (the pages size the partials in BF16, Table 2): the three calls
+ * of the single-pass key-tile kernel (at every D) with the dQ and dbias partials stored
+ * as bf16 — each partial element is the FP32 value rounded once to bf16 (round to
+ * nearest even) before it is stored; the reductions add the partials in FP32 in a fixed
+ * order.  Half the single-pass kernel's partial bytes, at the cost of one bf16 rounding
+ * per partial.  Buffers hold the element counts of tri_attn_workspace_single_pass, 2
+ * bytes each, 16-byte aligned.  The FP32 calls above remain the reference path.  Errors
+ * as for those calls.
  */
 tri_attn_status tri_attn_bwd_bf16p(const tri_attn_dims* d,
                                    const tri_bf16* q, const tri_bf16* k, const tri_bf16* v,
@@ -150,14 +160,17 @@ tri_attn_status tri_attn_reduce_dbias_bf16p(const tri_attn_dims* d, const tri_bf
 
 /*
  * Chunked backward with bounded partial memory (Figure 7(d): the pair-bias partial
- * buffers are reused once consumed; Table 2, column W_bias,res).  Does what
- * tri_attn_bwd, tri_attn_reduce_dq and tri_attn_reduce_dbias do together, over chunks of
- * C consecutive outer groups: the main backward of a chunk writes the chunk's dQ and
- * dbias partials into `workspace`, then one reduction kernel sums the chunk's dQ
+ * buffers are reused once consumed; Table 2, column W_bias,res), on the single-pass
+ * key-tile kernel at every D.  Does what that kernel and the two reductions do together,
+ * over chunks of C consecutive outer groups (outer groups, key tiles and partial counts
+ * of tri_attn_workspace_single_pass): the main backward of a chunk writes the chunk's dQ
+ * and dbias partials into `workspace`, then one reduction kernel sums the chunk's dQ
  * partials into its rows of dq and adds its dbias partials, in ascending group order, to
  * an FP32 running sum carried from chunk to chunk (rounded to bf16 into dbias after the
  * last chunk); the next chunk reuses the same buffers.  Every sum keeps the order of the
- * unchunked calls, so dq, dk, dv and dbias are bitwise those of the three calls.
+ * unchunked single-pass kernel and reductions, so results are bitwise the same for every
+ * chunk size, and, for D = 16 and 64 (where tri_attn_bwd is that kernel), bitwise those
+ * of the three calls; for D = 32 they equal the three calls up to summation order.
  *
  * C is the largest number of outer groups whose buffers fit in workspace_bytes (all
  * groups: a single chunk).  tri_attn_bwd_chunked_workspace gives the bytes a chunk of
@@ -207,15 +220,26 @@ tri_attn_status tri_attn_bwd_chunked_noalloc(const tri_attn_dims* d,
 int64_t tri_attn_noalloc_scratch_bytes(void);
 
 /*
- * Partial-buffer sizes for these dimensions (elements, FP32), the number of
- * key tiles J_K and of outer groups L, and the key-tile / group sizes used
- * (key tile 128; group G = 4 for D = 32, 6 for D = 16 with N even and 4 with N
- * odd, 2 for D = 64).  Any output pointer may be NULL.  Host-only arithmetic; no
- * device access.
+ * Partial-buffer sizes of tri_attn_bwd for these dimensions (elements, FP32), the number
+ * of dQ partials J_K and of dbias partials L, and the key-tile / outer-group sizes behind
+ * them.  D = 16, 64 (single-pass kernel): key tile 128; group G = 6 for D = 16 with N
+ * even, 4 with N odd, 2 for D = 64.  D = 32 (two kernels): the key range of the
+ * query-tile kernel (128, 256, 384, 512 or 768 keys; J_K = ceil(N / 768) ranges) and its
+ * outer group (L <= 64 groups).  Any output pointer may be NULL.  Host-only arithmetic;
+ * no device access.
  */
 tri_attn_status tri_attn_workspace(const tri_attn_dims* d, int64_t* dq_partial_elems,
                                    int64_t* dbias_partial_elems, int64_t* j_k, int64_t* l,
                                    int64_t* key_tile, int64_t* outer_group);
+
+/*
+ * The same sizes for the single-pass key-tile kernel that tri_attn_bwd_bf16p (and its two
+ * reductions) and the chunked backward use at every D: key tile 128, outer group G = 4 for
+ * D = 32, otherwise as above.
+ */
+tri_attn_status tri_attn_workspace_single_pass(const tri_attn_dims* d, int64_t* dq_partial_elems,
+                                               int64_t* dbias_partial_elems, int64_t* j_k, int64_t* l,
+                                               int64_t* key_tile, int64_t* outer_group);
 
 /* Human-readable name of a status code (static string). */
 const char* tri_attn_status_string(int status);   /* any int; unknown codes -> "unknown status" */

@@ -145,18 +145,40 @@ def test_workspace_matches_memory_table():
 
 
 def test_workspace_ragged():
-    """Partial counts for ragged shapes.  The outer group is 4 slices except on the direct-load
-    path with D = 16 (N even), where the smaller accumulators leave room for 6, and 2 slices for
-    D = 64, whose accumulators are twice as large."""
+    """Partial counts of the single-pass key-tile kernel for ragged shapes.  The outer group is
+    4 slices except on the direct-load path with D = 16 (N even), where the smaller accumulators
+    leave room for 6, and 2 slices for D = 64, whose accumulators are twice as large.  For
+    D = 16 and 64 the default backward is that kernel, so both queries agree."""
     from triangular_attention_amd import api
     for (N_o, N, D, G) in ((10, 65, 16, 4), (10, 64, 16, 6), (10, 66, 16, 6), (10, 64, 32, 4), (13, 200, 16, 6),
                            (13, 201, 32, 4), (13, 200, 64, 2), (13, 201, 64, 2)):
-        ws = api.workspace(_dims(B=2, N_o=N_o, H=3, N=N, D=D))
+        d = _dims(B=2, N_o=N_o, H=3, N=N, D=D)
+        ws = api.workspace(d, single_pass=True)
         jk, L = -(-N // ws["key_tile"]), -(-N_o // G)
         assert ws["outer_group"] == G and ws["key_tile"] == 128
         assert ws["j_k"] == jk and ws["l"] == L
         assert ws["dq_partial_elems"] == jk * 2 * N_o * 3 * N * D
         assert ws["dbias_partial_elems"] == L * 2 * 3 * N * N
+        if D != 32:
+            assert api.workspace(d) == ws
+
+
+@pytest.mark.parametrize("B,N_o,H,N,kr,J", [(1, 768, 4, 768, 768, 1), (1, 384, 4, 384, 384, 1),
+                                            (1, 1024, 4, 1024, 512, 2), (2, 5, 2, 100, 128, 1),
+                                            (1, 3, 1, 300, 384, 1), (1, 2, 1, 500, 512, 1),
+                                            (1, 2, 1, 800, 512, 2), (1, 1, 1, 1, 128, 1),
+                                            (1, 70, 1, 40, 128, 1), (1, 9, 3, 2000, 768, 3)])
+def test_workspace_two_kernel_plan(B, N_o, H, N, kr, J):
+    """D = 32: the query-tile kernel's plan.  J = ceil(N / 768) key ranges of the smallest range
+    (128, 256, 384, 512 or 768 keys) that covers N / J, one FP32 dQ partial per range and one FP32
+    dbias partial per outer group, at most 64 groups of equal size (the last one ragged)."""
+    from triangular_attention_amd import api
+    ws = api.workspace(_dims(B=B, N_o=N_o, H=H, N=N, D=32))
+    assert ws["key_tile"] == kr and ws["j_k"] == J and J * kr >= N
+    gs, L = ws["outer_group"], ws["l"]
+    assert 1 <= L <= min(64, N_o) and L == -(-N_o // gs) and (L - 1) * gs < N_o
+    assert ws["dq_partial_elems"] == J * B * N_o * H * N * 32
+    assert ws["dbias_partial_elems"] == L * B * H * N * N
 
 
 # --------------------------------------------------------------------------- block ABI
@@ -320,7 +342,7 @@ def test_chunked_workspace_sizes(lib, B, N_o, H, N, D):
     B * H * N * N, all FP32 and each rounded up to 256 bytes; C is clamped to 1..L."""
     from triangular_attention_amd import api
     d = _dims(B=B, N_o=N_o, H=H, N=N, D=D)
-    ws = api.workspace(d)
+    ws = api.workspace(d, single_pass=True)
     G, L, jk = ws["outer_group"], ws["l"], ws["j_k"]
     up = lambda x: -(-x // 256) * 256
     for C in (1, 2, 3, L - 1, L, L + 5):

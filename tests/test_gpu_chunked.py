@@ -1,9 +1,11 @@
 """The chunked backward (tri_attn_bwd_chunked; TurboPairFormer, Figure 7(d) and Table 2:
 partial buffers reused once consumed, so only one chunk of outer groups has partials at a
-time): bitwise equal to the three unchunked calls for every chunk size, including ragged last
-chunks, ragged last outer groups, B > 1, odd N (scalar reduction path), D = 16 (outer group
-6) and D = 64 (outer group 2); and at full size, where it is also checked against the oracle
-on sampled outputs.
+time) runs the single-pass key-tile kernel.  For every chunk size it is bitwise equal to the
+same kernel run as one chunk (all outer groups) and, for D = 16 and 64, whose default
+backward is that kernel, to the three unchunked calls; including ragged last chunks, ragged
+last outer groups, B > 1, odd N (scalar reduction path), D = 16 (outer group 6) and D = 64
+(outer group 2); and at full size, where it is also checked against the oracle on sampled
+outputs.
 """
 import numpy as np
 import pytest
@@ -23,9 +25,14 @@ def _bits(t):
 
 
 def _both(ta, dev, scale, chunk_groups):
+    """The chunked backward at each chunk size, and its reference: the same kernel as one chunk
+    (D = 32), or the three unchunked calls (D = 16, 64: the same kernel)."""
     o, o_res, lse = ta.forward(dev["q"], dev["k"], dev["v"], dev["bias"], dev["mask"], scale)
     args = (dev["q"], dev["k"], dev["v"], dev["bias"], dev["mask"], scale, o, o_res, lse, dev["do"])
-    ref = ta.backward(*args)
+    if dev["q"].shape[-1] == 32:
+        ref = ta.backward_chunked(*args)          # one chunk of all outer groups
+    else:
+        ref = ta.backward(*args)
     out = {}
     for C in chunk_groups:
         d = ta.dims_of(dev["q"], scale)
@@ -54,7 +61,7 @@ def test_chunked_bitwise_equals_unchunked(case):
     w, _ = workload(N_o, N, H, D, mask_p, bstd, B=B)
     x = inputs(w, seed=N + 3 * D, mask_p=mask_p)
     dev = to_dev(x)
-    L = ta.workspace(ta.dims_of(dev["q"], w.scale))["l"]
+    L = ta.workspace(ta.dims_of(dev["q"], w.scale), single_pass=True)["l"]
     sizes = sorted({1, 2, max(1, L - 1), L})
     print(f"chunked {case}: L = {L}, chunk sizes {sizes}", flush=True)
     ref, out = _both(ta, dev, w.scale, sizes)

@@ -1,9 +1,10 @@
 """The allocation-free backward (tri_attn_bwd_chunked_noalloc): its chunk buffers live in the
-library's static scratch array.  Checked through the C ABI against the existing entry points
-that take a caller workspace (tri_attn_bwd_chunked) and caller partial buffers (tri_attn_bwd +
-the two reductions): bitwise equal, on two calls in a row (the second with a smaller input, so
-the scratch holds the first call's contents when the second starts), then the full-size case
-against the oracle on sampled outputs."""
+library's static scratch array.  Checked through the C ABI against the entry point it is a
+variant of, which takes a caller workspace (tri_attn_bwd_chunked): bitwise equal, on two calls
+in a row (the second with a smaller input, so the scratch holds the first call's contents when
+the second starts).  Both run the single-pass key-tile kernel; the default five calls
+(tri_attn_bwd + the two reductions, two kernels at D = 32) give the same gradients up to
+rounding order, which is checked too, and the small case is checked against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -73,7 +74,9 @@ def test_noalloc_matches_workspace_entry_points_twice():
         for n, a, b, c in zip(("dq", "dk", "dv", "dbias"), got, ref_ws, ref):
             assert torch.isfinite(a.float()).all(), n
             assert torch.equal(_bits(a), _bits(b)), n
-            assert torch.equal(_bits(a), _bits(c)), n
+            # the default calls: same gradients, other summation order (dK, dV: same kernel code)
+            rel = float(((a.float() - c.float()).norm() / c.float().norm().clamp_min(1e-30)))
+            assert rel <= 4e-3, (n, rel)
         if w.N <= 100:
             # the small case whole against the oracle
             r = oracle.backward(x["q"], x["k"], x["v"], x["bias"], x["mask"], w.scale, x["do"])

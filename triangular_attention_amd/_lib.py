@@ -40,6 +40,7 @@ EXPORTS = (
     "tri_attn_bwd_chunked_noalloc",
     "tri_attn_noalloc_scratch_bytes",
     "tri_attn_workspace",
+    "tri_attn_workspace_single_pass",
     "tri_attn_status_string",
     "tri_attn_version",
 )
@@ -138,6 +139,7 @@ def load() -> ctypes.CDLL:
         "tri_attn_reduce_dq_bf16p": [dp, vp, vp, vp],
         "tri_attn_reduce_dbias_bf16p": [dp, vp, vp, vp],
         "tri_attn_workspace": [dp, i64p, i64p, i64p, i64p, i64p, i64p],
+        "tri_attn_workspace_single_pass": [dp, i64p, i64p, i64p, i64p, i64p, i64p],
         "tri_attn_bwd_chunked_workspace": [dp, ctypes.c_int64, i64p, i64p],
         "tri_attn_bwd_chunked": [dp] + [vp] * 13 + [ctypes.c_int64, vp],
         "tri_attn_bwd_chunked_noalloc": [dp] + [vp] * 13,

@@ -52,11 +52,14 @@ def dims_of(q: torch.Tensor, scale: float) -> _lib.Dims:
     return _lib.dims(B, N_o, H, N, D, scale)
 
 
-def workspace(d: _lib.Dims) -> dict:
-    """Partial-buffer sizes (``tri_attn_workspace``); host-only, no device access."""
+def workspace(d: _lib.Dims, single_pass: bool = False) -> dict:
+    """Partial-buffer sizes of the default backward (``tri_attn_workspace``) or, with
+    ``single_pass``, of the single-pass key-tile kernel behind the bf16-partial variant and the
+    chunked backward (``tri_attn_workspace_single_pass``); host-only, no device access."""
     lib = _lib.load()
     vals = [ctypes.c_int64() for _ in range(6)]
-    _lib.check("tri_attn_workspace", lib.tri_attn_workspace(ctypes.byref(d), *[ctypes.byref(v) for v in vals]))
+    name = "tri_attn_workspace_single_pass" if single_pass else "tri_attn_workspace"
+    _lib.check(name, getattr(lib, name)(ctypes.byref(d), *[ctypes.byref(v) for v in vals]))
     keys = ("dq_partial_elems", "dbias_partial_elems", "j_k", "l", "key_tile", "outer_group")
     return {k: v.value for k, v in zip(keys, vals)}
 
@@ -111,7 +114,7 @@ def tri_attn_bwd(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv, dq_partial, db
         _need(mask, "mask", torch.float32, (B, N_o, N))
     _need(lse, "lse", torch.float32, (B, N_o, H, N))
     _need(delta, "delta", torch.float32, (B, N_o, H, N))
-    ws = workspace(d)
+    ws = workspace(d, single_pass=bf16_partials)
     pdt = _partial_dtype(bf16_partials)
     _need_partial(dq_partial, "dq_partial", pdt, ws["dq_partial_elems"])
     _need_partial(dbias_partial, "dbias_partial", pdt, ws["dbias_partial_elems"])
@@ -125,7 +128,8 @@ def tri_attn_bwd(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv, dq_partial, db
 def tri_attn_reduce_dq(d, dq_partial, dq, stream=None, bf16_partials=False):
     """dQ from its partials; ``bf16_partials`` selects ``tri_attn_reduce_dq_bf16p``."""
     _need(dq, "dq", torch.bfloat16, (d.B, d.N_o, d.H, d.N, d.D))
-    _need_partial(dq_partial, "dq_partial", _partial_dtype(bf16_partials), workspace(d)["dq_partial_elems"])
+    _need_partial(dq_partial, "dq_partial", _partial_dtype(bf16_partials),
+                  workspace(d, single_pass=bf16_partials)["dq_partial_elems"])
     lib = _lib.load()
     name = "tri_attn_reduce_dq_bf16p" if bf16_partials else "tri_attn_reduce_dq"
     _lib.check(name, getattr(lib, name)(ctypes.byref(d), _ptr(dq_partial), _ptr(dq), _stream(stream)))
@@ -134,7 +138,8 @@ def tri_attn_reduce_dq(d, dq_partial, dq, stream=None, bf16_partials=False):
 def tri_attn_reduce_dbias(d, dbias_partial, dbias, stream=None, bf16_partials=False):
     """dbias from its partials; ``bf16_partials`` selects ``tri_attn_reduce_dbias_bf16p``."""
     _need(dbias, "dbias", torch.bfloat16, (d.B, d.H, d.N, d.N))
-    _need_partial(dbias_partial, "dbias_partial", _partial_dtype(bf16_partials), workspace(d)["dbias_partial_elems"])
+    _need_partial(dbias_partial, "dbias_partial", _partial_dtype(bf16_partials),
+                  workspace(d, single_pass=bf16_partials)["dbias_partial_elems"])
     lib = _lib.load()
     name = "tri_attn_reduce_dbias_bf16p" if bf16_partials else "tri_attn_reduce_dbias"
     _lib.check(name, getattr(lib, name)(ctypes.byref(d), _ptr(dbias_partial), _ptr(dbias), _stream(stream)))
@@ -210,7 +215,7 @@ def backward(q, k, v, bias, mask, scale, o, o_res, lse, d_o, workspace_buffers=N
     """Delta, key-tile backward and the two reductions.  Returns ``(dq, dk, dv, dbias)``.
     ``bf16_partials`` runs the bf16-partial variant (half the partial bytes)."""
     d = dims_of(q, scale)
-    ws = workspace(d)
+    ws = workspace(d, single_pass=bf16_partials)
     delta = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     tri_attn_bwd_delta(d, o, o_res, d_o, delta)
     if workspace_buffers is None:
@@ -237,7 +242,7 @@ def backward_chunked(q, k, v, bias, mask, scale, o, o_res, lse, d_o, groups_per_
     None) unless one is given.  Returns ``(dq, dk, dv, dbias)``, bitwise those of ``backward``."""
     d = dims_of(q, scale)
     if buffer is None:
-        n = workspace(d)["l"] if groups_per_chunk is None else groups_per_chunk
+        n = workspace(d, single_pass=True)["l"] if groups_per_chunk is None else groups_per_chunk
         buffer = torch.empty(chunked_workspace(d, n)["bytes"], dtype=torch.uint8, device=q.device)
     delta = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     tri_attn_bwd_delta(d, o, o_res, d_o, delta)

@@ -16,7 +16,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libtri_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "delta_reduce.hip", "block.hip", "block_api.hip", "trimul.hip",
+SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "bwd_q.hip", "delta_reduce.hip", "block.hip", "block_api.hip", "trimul.hip",
            "trimul_api.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -32,6 +32,7 @@ FLAGS = [
 EXTRA = {
     "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "bwd_q.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

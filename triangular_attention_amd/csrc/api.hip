@@ -38,6 +38,14 @@ int64_t n_groups(const tri_attn_dims* d) { return (d->N_o + group_size(d) - 1) /
 int64_t x_elems(const tri_attn_dims* d) { return d->B * d->N_o * d->H * d->N * d->D; }
 int64_t y_elems(const tri_attn_dims* d) { return d->B * d->H * d->N * d->N; }
 
+// The default FP32 backward runs as two kernels for D = 32 (the key-tile kernel for dK, dV
+// and the query-tile kernel for dQ, dbias); D = 16 and 64, the bf16-partial variant and the
+// chunked backward use the single-pass key-tile kernel.  Partial counts of each design:
+bool two_kernel(const tri_attn_dims* d) { return d->D == 32; }
+tri::BwdQPlan q_plan(const tri_attn_dims* d) { return tri::bwdq_plan(d->B, d->N_o, d->H, d->N); }
+int64_t dq_parts(const tri_attn_dims* d) { return two_kernel(d) ? q_plan(d).n_ranges : n_key_tiles(d); }
+int64_t db_parts(const tri_attn_dims* d) { return two_kernel(d) ? q_plan(d).n_groups : n_groups(d); }
+
 tri_attn_status launched(hipError_t e) { return e == hipSuccess ? TRI_ATTN_OK : TRI_ATTN_ERR_LAUNCH; }
 
 }  // namespace
@@ -63,6 +71,22 @@ const char* tri_attn_version(void) { return "0.1.0"; }
 tri_attn_status tri_attn_workspace(const tri_attn_dims* d, int64_t* dq_partial_elems,
                                    int64_t* dbias_partial_elems, int64_t* j_k, int64_t* l,
                                    int64_t* key_tile, int64_t* outer_group) {
+  tri_attn_status st = check_dims(d);
+  if (st != TRI_ATTN_OK) return st;
+  const bool two = two_kernel(d);
+  const tri::BwdQPlan p = two ? q_plan(d) : tri::BwdQPlan();
+  if (dq_partial_elems) *dq_partial_elems = dq_parts(d) * x_elems(d);
+  if (dbias_partial_elems) *dbias_partial_elems = db_parts(d) * y_elems(d);
+  if (j_k) *j_k = dq_parts(d);
+  if (l) *l = db_parts(d);
+  if (key_tile) *key_tile = two ? p.kr : tri::kBwdKeyTile;
+  if (outer_group) *outer_group = two ? p.gs : group_size(d);
+  return TRI_ATTN_OK;
+}
+
+tri_attn_status tri_attn_workspace_single_pass(const tri_attn_dims* d, int64_t* dq_partial_elems,
+                                               int64_t* dbias_partial_elems, int64_t* j_k, int64_t* l,
+                                               int64_t* key_tile, int64_t* outer_group) {
   tri_attn_status st = check_dims(d);
   if (st != TRI_ATTN_OK) return st;
   if (dq_partial_elems) *dq_partial_elems = n_key_tiles(d) * x_elems(d);
@@ -118,6 +142,7 @@ tri::BwdArgs bwd_args(const tri_attn_dims* d, const tri_bf16* q, const tri_bf16*
   a.lse = lse; a.delta = delta; a.dk = dk; a.dv = dv;
   a.dq_partial = nullptr; a.dbias_partial = nullptr;
   a.bf16_partials = 0;
+  a.kv_only = 0;
   a.B = (int)d->B; a.N_o = (int)d->N_o; a.H = (int)d->H; a.N = (int)d->N;
   a.n_key_tiles = (int)n_key_tiles(d);
   a.g0 = 0;
@@ -134,8 +159,13 @@ tri_attn_status check_bwd_inputs(const tri_attn_dims* d, const tri_bf16* q, cons
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bias) || !aligned16(d_o) ||
       !aligned16(lse) || !aligned16(delta) || (mask && !aligned16(mask)))
     return TRI_ATTN_ERR_ALIGN;
-  // a launch has 8 * ceil(B * L * H / 8) * J_K workgroups (32-bit grid)
+  // a launch has 8 * ceil(B * L * H / 8) * J_K workgroups (32-bit grid), the query-tile
+  // kernel 8 * ceil(B * H * J * L / 8) * ceil(N / 32)
   if (n_key_tiles(d) * (d->H * n_groups(d) * d->B + 7) > 0x7fffffff) return TRI_ATTN_ERR_SHAPE;
+  if (two_kernel(d)) {
+    const tri::BwdQPlan p = q_plan(d);
+    if ((d->B * d->H * p.n_ranges * p.n_groups + 7) * p.n_qt > 0x7fffffff) return TRI_ATTN_ERR_SHAPE;
+  }
   return TRI_ATTN_OK;
 }
 
@@ -152,6 +182,21 @@ tri_attn_status bwd_impl(const tri_attn_dims* d, const tri_bf16* q, const tri_bf
   if (!aligned16(dk) || !aligned16(dv) || !aligned16(dq_partial) || !aligned16(dbias_partial))
     return TRI_ATTN_ERR_ALIGN;
   tri::BwdArgs a = bwd_args(d, q, k, v, bias, mask, d_o, lse, delta, dk, dv);
+  if (!bf16_partials && two_kernel(d)) {
+    // dK, dV from the key-tile kernel; dQ and dbias partials from the query-tile kernel
+    a.kv_only = 1;
+    hipError_t e = tri::launch_bwd(a, (int)d->D, (hipStream_t)stream);
+    if (e != hipSuccess) return TRI_ATTN_ERR_LAUNCH;
+    tri::BwdQArgs qa;
+    qa.q = q; qa.k = k; qa.v = v; qa.bias = bias; qa.mask = mask; qa.d_o = d_o;
+    qa.lse = lse; qa.delta = delta;
+    qa.dq_partial = static_cast<float*>(dq_partial);
+    qa.dbias_partial = static_cast<float*>(dbias_partial);
+    qa.B = (int)d->B; qa.N_o = (int)d->N_o; qa.H = (int)d->H; qa.N = (int)d->N;
+    qa.p = q_plan(d);
+    qa.scale = d->scale;
+    return launched(tri::launch_bwdq(qa, (int)d->D, (hipStream_t)stream));
+  }
   a.dq_partial = dq_partial; a.dbias_partial = dbias_partial;
   a.bf16_partials = bf16_partials;
   return launched(tri::launch_bwd(a, (int)d->D, (hipStream_t)stream));
@@ -292,7 +337,9 @@ tri_attn_status reduce_impl(const tri_attn_dims* d, const void* partial, tri_bf1
   tri::ReduceArgs a;
   a.partial = partial; a.out = out;
   a.elems = dq ? x_elems(d) : y_elems(d);
-  a.n_partials = (int)(dq ? n_key_tiles(d) : n_groups(d));
+  // FP32 partials: the default design's counts; bf16 partials: the single-pass kernel's
+  if (bf16_partials) a.n_partials = (int)(dq ? n_key_tiles(d) : n_groups(d));
+  else a.n_partials = (int)(dq ? dq_parts(d) : db_parts(d));
   a.bf16_partials = bf16_partials;
   return launched(tri::launch_reduce(a, (hipStream_t)stream));
 }

@@ -45,97 +45,26 @@
 // the row's low bits (conflict-free transposing reads).
 #include "common.h"
 #include "kernels.h"
+#include "bwd_layout.h"
 
 namespace tri {
-
-// Element offset of (row, col) in the LDS tiles.  D = 32: unpadded rows, chunk
-// XOR swizzle: Q/dO by row bits 3-4, K by row bits 2-3.  D = 16: rows padded
-// to 24 elements.
-template <int D> struct Lay;
-template <> struct Lay<32> {
-  static constexpr int kRowElems = 32;
-  static constexpr int kKVRowElems = 32;
-  __device__ static __forceinline__ int swq(int row) { return ((row >> 3) & 1) << 1 | ((row >> 4) & 1); }
-  __device__ static __forceinline__ int swk(int row) { return (row >> 2) & 3; }
-  __device__ static __forceinline__ int q(int row, int col) {
-    return row * 32 + ((((col >> 3) ^ swq(row)) & 3) << 3) + (col & 7);
-  }
-  __device__ static __forceinline__ int k(int row, int col) {
-    return row * 32 + ((((col >> 3) ^ swk(row)) & 3) << 3) + (col & 7);
-  }
-  __device__ static __forceinline__ int v(int row, int col) { return q(row, col); }
-  // logical chunk stored in physical slot `pchunk` of `row`
-  __device__ static __forceinline__ int q_src_chunk(int row, int pchunk) { return (pchunk ^ swq(row)) & 3; }
-  static constexpr int kSlotsPerRow = 4;
-};
-template <> struct Lay<16> {
-  static constexpr int kRowElems = 24;       // Q / dO rows padded to 48 bytes
-  static constexpr int kKVRowElems = 16;     // K / V rows unpadded (32 bytes)
-  __device__ static __forceinline__ int q(int row, int col) { return row * 24 + col; }
-  // K and V: in every 16-row group rows 8..11 and 12..15 trade places (row bit 2
-  // flipped where bit 3 is set) and the four 8-byte units of those rows are
-  // permuted by an XOR with 2, so that both the row reads (16 rows x 2 units per
-  // half-wave) and the transposing reads (rows 0..3 and 8..11 of a 16-row group)
-  // touch 64 distinct banks
-  __device__ static __forceinline__ int k(int row, int col) {
-    const int hi = (row >> 3) & 1;
-    return (row ^ (hi << 2)) * 16 + ((((col >> 2) ^ (hi << 1)) & 3) << 2) + (col & 3);
-  }
-  __device__ static __forceinline__ int v(int row, int col) { return k(row, col); }
-  __device__ static __forceinline__ int q_src_chunk(int row, int pchunk) { return pchunk < 2 ? pchunk : 0; }
-  static constexpr int kSlotsPerRow = 3;     // two data chunks and one padding chunk
-};
-
-// D = 64: unpadded 128-byte rows of eight 16-byte chunks, the chunk index XORed with a
-// row-dependent value.  Per half-wave, the score-product row reads touch four rows of
-// equal (row mod 4) at two chunks each (Q / dO: rows differing in bits 3-4; K / V: bits
-// 2-3) and the transposing reads four rows of equal parity at two chunks each (bits 1
-// and 3); the XOR values below give every such set eight distinct 16-byte positions
-// (and distinct 8-byte units for the transposing reads).
-template <> struct Lay<64> {
-  static constexpr int kRowElems = 64;
-  static constexpr int kKVRowElems = 64;
-  __device__ static __forceinline__ int swq(int row) {
-    return (((row >> 1) & 1) * 2) ^ (((row >> 3) & 1) * 5) ^ (((row >> 4) & 1) * 4);
-  }
-  __device__ static __forceinline__ int swk(int row) {
-    return (((row >> 1) & 1) * 2) ^ (((row >> 2) & 1) * 4) ^ (((row >> 3) & 1) * 5);
-  }
-  __device__ static __forceinline__ int q(int row, int col) {
-    return row * 64 + ((((col >> 3) ^ swq(row)) & 7) << 3) + (col & 7);
-  }
-  __device__ static __forceinline__ int k(int row, int col) {
-    return row * 64 + ((((col >> 3) ^ swk(row)) & 7) << 3) + (col & 7);
-  }
-  __device__ static __forceinline__ int v(int row, int col) { return k(row, col); }
-  __device__ static __forceinline__ int q_src_chunk(int row, int pchunk) { return (pchunk ^ swq(row)) & 7; }
-  static constexpr int kSlotsPerRow = 8;
-};
-
-// One lane's contraction operand (DOp<D>::T) from an LDS tile: D / 4 elements from
-// column col of row row; with D = 64 its two 16-byte chunks sit at their own swizzled
-// positions.
-template <int D, typename F>
-__device__ __forceinline__ typename DOp<D>::T ld_op(const uint16_t* t, int row, int col, F at) {
-  if constexpr (D == 64) {
-    typename DOp<D>::T r;
-    r.x[0] = ld_shared<u32x4>(&t[at(row, col)]);
-    r.x[1] = ld_shared<u32x4>(&t[at(row, col + 8)]);
-    return r;
-  } else {
-    return ld_shared<typename DOp<D>::T>(&t[at(row, col)]);
-  }
-}
 
 // LD: how the bias tile reaches LDS.  16: 16-byte direct loads (N % 8 == 0); 4: 4-byte
 // direct loads, one per 256-byte bias row (N even); 0: through registers (N odd).
 // BP: dQ and dbias partials stored as bf16 (one RNE rounding each) instead of FP32.
-template <int D, bool MASK, int LD, bool BP, int TK>
-__global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
+// KV: dK and dV only (no dQ product, no dbias tile, no partials); the query-tile
+// kernel of bwd_q.hip computes dQ and dbias.
+// TK: keys per workgroup, 16 per wave: 128 (8 waves, one workgroup per CU), or 64 for the
+// dK/dV-only variant with D = 32 on the 16-byte load path.  That variant also takes outer
+// groups of 2 slices and 32-query stages: without the dQ and dbias work it then needs 127
+// VGPRs and 37 KB of LDS, so four workgroups (16 waves) share a CU and their stage barriers
+// fall at independent times (at N = 768: 1.15 -> 0.87 ms against 8-wave workgroups).
+template <int D, bool MASK, int LD, bool BP, int TK, bool KV>
+__global__ __launch_bounds__(TK * 4, TK == 64 ? 3 : 1) void bwd_kernel(BwdArgs a) {
   constexpr bool VEC = LD != 0;   // direct global->LDS path
   constexpr int NW = TK / 16;     // waves; wave w owns keys 16w..16w+15 of the tile
   constexpr int NT = NW * 64;
-  constexpr int TQ = bwd_query_tile(D), G = bwd_group(D, VEC);
+  constexpr int TQ = TK == 64 ? 32 : bwd_query_tile(D), G = TK == 64 ? 2 : bwd_group(D, VEC);
   constexpr int NQB = TQ / 16;    // 16-query blocks of a stage
   constexpr int NST = TQ / 32;    // 32-query halves of a stage (dV / dK contraction steps)
   static_assert(TQ % 32 == 0, "query tile must be whole 32-query halves");
@@ -154,7 +83,8 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int NR = (2 * NQCH + NT - 1) / NT;
   constexpr int NRB = (NBCH + NT - 1) / NT;
   constexpr int NBLK = NQB * NDB; // dQ output blocks per stage
-  static_assert(NBLK <= NW, "one dQ block per wave at most");
+  static_assert(KV || NBLK <= NW, "one dQ block per wave at most");
+  static_assert(TK == 128 || (TK == 64 && KV && LD == 16 && D == 32), "64-key tiles: dK/dV only, D = 32, 16-byte loads");
   typedef typename DOp<D>::T QT;
   constexpr int QL = DOp<D>::kPerLane;
 
@@ -162,7 +92,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) uint16_t sdO[NB][TQ * RE];
   __shared__ __align__(16) float sL[NB][TQ];    // -lse / scale of the stage's rows
   __shared__ __align__(16) float sDl[NB][TQ];   // -delta
-  __shared__ __align__(16) uint16_t sdS[2][TK * SP];
+  __shared__ __align__(16) uint16_t sdS[KV ? 1 : 2][KV ? 8 : TK * SP];
   __shared__ __align__(16) uint16_t sK[G][TK * KRE];
   __shared__ __align__(16) uint16_t sV[G][TK * KRE];   // V rows of the key tile (row-read layout)
   __shared__ __align__(16) uint16_t sB[2][TQ * TK];
@@ -252,12 +182,14 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr int SPR = Lay<D>::kSlotsPerRow;
   constexpr int NQPIECE = TQ * SPR / 64;
   static_assert(TQ * SPR % 64 == 0, "Q tile must be whole wave pieces");
-  static_assert(!VEC || NQPIECE <= HW, "one Q and one dO piece per wave of a loader set");
+  constexpr int NQPW = (NQPIECE + HW - 1) / HW;   // Q (and dO) pieces per wave of a loader set
+  static_assert(!VEC || NQPW == 1 || TK == 64, "one Q and one dO piece per wave of a loader set");
   const int lset = w / HW, ws = w % HW;     // loader set of the wave, wave index within it
-  uint32_t qoff;
-  {
-    const int slot = ws * 64 + lane, row = slot / SPR, ch = Lay<D>::q_src_chunk(row, slot % SPR);
-    qoff = (uint32_t)(row * D + ch * 8) * 2;
+  uint32_t qoff[NQPW];                      // wave ws loads pieces ws, ws + HW, ..
+#pragma unroll
+  for (int k = 0; k < NQPW; ++k) {
+    const int slot = (ws + k * HW) * 64 + lane, row = slot / SPR, ch = Lay<D>::q_src_chunk(row, slot % SPR);
+    qoff[k] = (uint32_t)(row * D + ch * 8) * 2;
   }
   // -lse/scale and -delta of a stage: lanes 0..15 fetch 4 lse values each, lanes
   // 16..31 4 delta values (direct path: first wave of the loading set; register path: wave 0)
@@ -295,9 +227,13 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
     const int64_t sr = srow(gg) + (int64_t)jj * TQ;     // first row of the tile
     const bool live = gg < nsl;
     const uint32_t ext = live ? (uint32_t)(N - jj * TQ) * D * 2 : 0u;
-    if (ws < NQPIECE) {
-      dma16(make_rsrc_words(a.q + sr * D, ext), sQ[buf] + ws * 512, qoff);
-      dma16(make_rsrc_words(a.d_o + sr * D, ext), sdO[buf] + ws * 512, qoff);
+#pragma unroll
+    for (int k = 0; k < NQPW; ++k) {
+      const int piece = ws + k * HW;
+      if (piece < NQPIECE) {
+        dma16(make_rsrc_words(a.q + sr * D, ext), sQ[buf] + piece * 512, qoff[k]);
+        dma16(make_rsrc_words(a.d_o + sr * D, ext), sdO[buf] + piece * 512, qoff[k]);
+      }
     }
     load_rls(sr, jj, live);
   };
@@ -335,9 +271,13 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   // ---- bias tile of (query tile j, key tile t), staged [query][key]: 256-byte rows,
   // 8-byte unit u of row r stored at unit position u ^ bsw(r) (bsw even, so 16-byte
   // chunks stay whole for the direct loads)
-  static_assert(TK == 128, "bias tile layout assumes 128 keys");
-  auto bsw = [](int r) { return ((r & 3) << 2) | (((r >> 3) & 1) << 4); };
-  auto b_at = [&](int r, int key) { return 128 * r + 4 * ((key >> 2) ^ bsw(r)) + (key & 3); };
+  // 64-key tiles: 128-byte rows, unit position u ^ bsw(r) with bsw from row bits 1 and 3,
+  // so the transposing reads of a half-wave (rows r0 + 0..3 and r0 + 8..11, four units
+  // each) cover all 64 banks
+  auto bsw = [](int r) {
+    return TK == 128 ? (((r & 3) << 2) | (((r >> 3) & 1) << 4)) : ((((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 3));
+  };
+  auto b_at = [&](int r, int key) { return TK * r + 4 * ((key >> 2) ^ bsw(r)) + (key & 3); };
   constexpr int BCH = TK / 8;                    // 16-byte slots per bias row
   constexpr int NBPIECE = TQ * BCH / 64;
   static_assert(TQ * BCH % 64 == 0, "bias tile must be whole wave pieces");
@@ -434,7 +374,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   constexpr bool DSET = VEC;
   constexpr bool DEARLY = VEC && D == 64;   // dbias stores split around the last stage's barrier
   constexpr int DQB = DSET ? NBLK / HW : 1;     // dQ blocks per computing wave
-  static_assert(!DSET || (NBLK % HW == 0 && NDB % DQB == 0), "a wave's dQ blocks share one query block");
+  static_assert(KV || !DSET || (NBLK % HW == 0 && NDB % DQB == 0), "a wave's dQ blocks share one query block");
   auto dq_blocks = [&](int jj, int gg, int buf, bool store, int blk0) {
     const int qb = blk0 / NDB;
     const uint16_t* kt_tile = sK[gg];
@@ -478,7 +418,8 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
   };
   // dset: the loader set that does not wait at the end of the current stage
   auto dq_stage = [&](int jj, int gg, int buf, bool store, int dset) {
-    if constexpr (DSET) {
+    if constexpr (KV) {
+    } else if constexpr (DSET) {
       if (lset == dset) dq_blocks(jj, gg, buf, store, ws * DQB);
     } else {
       if (w < NBLK) dq_blocks(jj, gg, buf, store, w);
@@ -605,10 +546,12 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
             p[i] = __builtin_amdgcn_exp2f(x);
             ds[i] = p[i] * dp[i];
           }
-          if (gs == 0) {
-            dbacc[qb] = f32x4{ds[0], ds[1], ds[2], ds[3]};
-          } else if (FULL || gs < nsl) {
-            dbacc[qb] += f32x4{ds[0], ds[1], ds[2], ds[3]};
+          if constexpr (!KV) {
+            if (gs == 0) {
+              dbacc[qb] = f32x4{ds[0], ds[1], ds[2], ds[3]};
+            } else if (FULL || gs < nsl) {
+              dbacc[qb] += f32x4{ds[0], ds[1], ds[2], ds[3]};
+            }
           }
           pP[e] = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
           pS[e] = u32x2{pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3])};
@@ -616,7 +559,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries of this half
         const u32x4 bp = u32x4{pP[0][0], pP[0][1], pP[1][0], pP[1][1]};
         const u32x4 bs = u32x4{pS[0][0], pS[0][1], pS[1][0], pS[1][1]};
-        *reinterpret_cast<u32x4*>(&sdS[dsb][(16 * w + c) * SP + 32 * st + 8 * g]) = bs;
+        if constexpr (!KV) *reinterpret_cast<u32x4*>(&sdS[dsb][(16 * w + c) * SP + 32 * st + 8 * g]) = bs;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int qr = 32 * st + 8 * g + trk, qc = 16 * db + 4 * tra;
@@ -634,7 +577,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
       // that set's own vmcnt(0); the other set stores it after the barrier, two stages before
       // its wait (measured at N = 768: 3.44 -> 2.96 ms; no gain for D = 16 and 32, where a
       // tile has four stages, so the stores stay after the barrier there)
-      if (DEARLY && gs == G - 1 && lset == (r & 1)) store_dbias();
+      if (!KV && DEARLY && gs == G - 1 && lset == (r & 1)) store_dbias();
       if (VEC) {
         // the set that loaded stage s+1 waits for it and stages its -lse/-delta; the
         // other set's loads (stage s+2) stay in flight across this barrier
@@ -663,7 +606,7 @@ __global__ __launch_bounds__(TK * 4) void bwd_kernel(BwdArgs a) {
         if (gs == G - 1 && j + 2 < nqt) load_bias_regs(j + 2);
       }
     }
-    if (!DEARLY || lset != ((R0 + G - 1) & 1)) store_dbias();
+    if (!KV && (!DEARLY || lset != ((R0 + G - 1) & 1))) store_dbias();
 
   };
   using R0a = std::integral_constant<int, 0>;
@@ -709,10 +652,25 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   constexpr int TK = kBwdKeyTile;
   const int64_t nunit = (int64_t)a.B * a.n_groups * a.H;
   const int64_t nblk = 8 * ((nunit + 7) / 8) * a.n_key_tiles;
-  if (a.bf16_partials)
-    hipLaunchKernelGGL((bwd_kernel<D, MASK, LD, true, TK>), dim3((unsigned)nblk), dim3(TK * 4), 0, s, a);
+  if (a.kv_only) {
+    // dK / dV only (the two-kernel backward, D = 32)
+    if constexpr (D != 32) {
+      return hipErrorInvalidValue;
+    } else if constexpr (LD == 16) {
+      // 64-key tiles over outer groups of 2 slices
+      BwdArgs k = a;
+      k.n_key_tiles = (a.N + 63) / 64;
+      k.n_groups = (a.N_o + 1) / 2;
+      const int64_t nu = (int64_t)a.B * k.n_groups * a.H;
+      const int64_t nb = 8 * ((nu + 7) / 8) * k.n_key_tiles;
+      hipLaunchKernelGGL((bwd_kernel<D, MASK, LD, false, 64, true>), dim3((unsigned)nb), dim3(256), 0, s, k);
+    } else {
+      hipLaunchKernelGGL((bwd_kernel<D, MASK, LD, false, TK, true>), dim3((unsigned)nblk), dim3(TK * 4), 0, s, a);
+    }
+  } else if (a.bf16_partials)
+    hipLaunchKernelGGL((bwd_kernel<D, MASK, LD, true, TK, false>), dim3((unsigned)nblk), dim3(TK * 4), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_kernel<D, MASK, LD, false, TK>), dim3((unsigned)nblk), dim3(TK * 4), 0, s, a);
+    hipLaunchKernelGGL((bwd_kernel<D, MASK, LD, false, TK, false>), dim3((unsigned)nblk), dim3(TK * 4), 0, s, a);
   return hipGetLastError();
 }
 

@@ -66,6 +66,7 @@ struct BwdArgs {
   int g0, n_groups, part_slices;
   float scale;
   int bf16_partials;     // 1: partials stored as bf16 (one RNE rounding each)
+  int kv_only;           // 1: dK and dV only (dq_partial, dbias_partial unused)
 };
 
 struct ReduceArgs {
@@ -96,7 +97,68 @@ struct SegReduceArgs {
   int njobs;
 };
 
+// Query-tile backward (dQ and dbias; bwd_q.hip).  A workgroup of nw waves owns 32 queries of
+// one head, one range of kr = 32 * np * nw keys (wave w: keys 32 * np * w ..) and one outer
+// group of gs consecutive slices, which it visits in ascending order: the dbias of its
+// (query, key) block accumulates over the group in FP32 registers (one partial per group),
+// and each slice's dQ over the range is complete in the workgroup (one partial per range).
+constexpr int kBwdQQueries = 32;
+constexpr int kBwdQMaxRange = 768;
+constexpr int kDeviceCUs = 256;          // MI355X compute units
+struct BwdQPlan {
+  int nw, np;         // waves per workgroup, 32-key pairs per wave
+  int n_ranges, kr;   // J key ranges of kr keys
+  int n_groups, gs;   // L outer groups of gs slices
+  int n_qt;           // 32-query tiles
+};
+inline BwdQPlan bwdq_plan(int64_t B, int64_t N_o, int64_t H, int64_t N) {
+  BwdQPlan p;
+  p.n_ranges = (int)((N + kBwdQMaxRange - 1) / kBwdQMaxRange);
+  const int64_t need = (N + p.n_ranges - 1) / p.n_ranges;
+  // smallest range that holds `need` keys: 128 (4 x 1), 256 (4 x 2), 384 (4 x 3), 512 (8 x 2), 768 (8 x 3)
+  static const int opt[5][2] = {{4, 1}, {4, 2}, {4, 3}, {8, 2}, {8, 3}};
+  int i = 0;
+  while (i < 4 && 32 * opt[i][0] * opt[i][1] < need) ++i;
+  p.nw = opt[i][0];
+  p.np = opt[i][1];
+  p.kr = 32 * p.nw * p.np;
+  p.n_qt = (int)((N + kBwdQQueries - 1) / kBwdQQueries);
+  // outer groups: fewest rounds of workgroups x slices per workgroup (plus a per-workgroup
+  // start-up of about 1.5 slices); workgroups per CU: 1 with 8 waves, 2 with 4
+  const int64_t slots = (int64_t)kDeviceCUs * (p.nw == 8 ? 1 : 2);
+  const int64_t units = B * H * p.n_ranges * p.n_qt;
+  double best = 0;
+  int bestL = 1;
+  const int64_t maxL = N_o < 64 ? N_o : 64;
+  for (int64_t L = 1; L <= maxL; ++L) {
+    const int64_t gs = (N_o + L - 1) / L;
+    const int64_t rounds = (units * L + slots - 1) / slots;
+    const double cost = (double)rounds * ((double)gs + 1.5);
+    if (L == 1 || cost < best) { best = cost; bestL = (int)L; }
+  }
+  p.gs = (int)((N_o + bestL - 1) / bestL);
+  p.n_groups = (int)((N_o + p.gs - 1) / p.gs);
+  return p;
+}
+
+struct BwdQArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* bias;
+  const float* mask;
+  const uint16_t* d_o;
+  const float* lse;
+  const float* delta;
+  float* dq_partial;      // [n_ranges, B, N_o, H, N, D]
+  float* dbias_partial;   // [n_groups, B, H, N, N]
+  int B, N_o, H, N;
+  BwdQPlan p;
+  float scale;
+};
+
 hipError_t launch_fwd(const FwdArgs& a, int D, hipStream_t s);
+hipError_t launch_bwdq(const BwdQArgs& a, int D, hipStream_t s);
 hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
