@@ -342,8 +342,9 @@ def sweep(args, dev):
         bwd = sum(v["ms"] for n, v in k.items() if n != "fwd")
         cb = r.get("cpu_baseline")
         ro = r["roofline"]
+        kname = ro["kernel"].split(" (")[0] + (" (2 kernels)" if "two kernels" in ro["kernel"] else "")
         print(f"| {r['config']['workload']} | {r['ms_per_step']:.3f} | {r['value']:.0f} | {r['pct_bf16_peak']:.1f} | "
-              f"{k['fwd']['ms']:.3f} | {bwd:.3f} | {ro['kernel']} | {ro['bound']} | {ro['frac']:.3f} | "
+              f"{k['fwd']['ms']:.3f} | {bwd:.3f} | {kname} | {ro['bound']} | {ro['frac']:.3f} | "
               + (f"{cb['value']:.3f} ({cb['cores']}) | {r['value'] / cb['value']:.0f}x |" if cb else "- | - |"))
 
 
