@@ -21,8 +21,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "triangular_attention_amd", "csrc")
 OUT = os.path.join(ROOT, "triangular_attention_amd", "_build", "sanitize")
 HIPCC = "/opt/rocm/bin/hipcc"
-SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "delta_reduce.hip", "block.hip", "block_api.hip", "trimul.hip",
-           "trimul_api.hip"]
+sys.path.insert(0, ROOT)
+from triangular_attention_amd.build import SOURCES  # noqa: E402  (the library's own source list)
 # each sanitizer flag applies to the host pass only
 HOST_SANITIZE = ["-Xarch_host -fsanitize=address", "-Xarch_host -fsanitize=undefined",
                  "-Xarch_host -fno-sanitize-recover=undefined", "-Xarch_host -fno-omit-frame-pointer"]
@@ -39,7 +39,7 @@ def _sources_hash():
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
         h.update(f.encode() + open(os.path.join(CSRC, f), "rb").read())
-    h.update(" ".join(FLAGS + HOST_SANITIZE).encode())
+    h.update(" ".join(FLAGS + HOST_SANITIZE + list(SOURCES)).encode())
     return h.hexdigest()[:16]
 
 

@@ -191,36 +191,33 @@ __global__ __launch_bounds__(TK * 4, TK == 64 ? 3 : 1) void bwd_kernel(BwdArgs a
     const int slot = (ws + k * HW) * 64 + lane, row = slot / SPR, ch = Lay<D>::q_src_chunk(row, slot % SPR);
     qoff[k] = (uint32_t)(row * D + ch * 8) * 2;
   }
-  // -lse/scale and -delta of a stage: lanes 0..15 fetch 4 lse values each, lanes
-  // 16..31 4 delta values (direct path: first wave of the loading set; register path: wave 0)
-  const bool rls_lane = (VEC ? ws == 0 : w == 0) && lane < 2 * TQ / 4;
+  // -lse/scale and -delta of a stage: lanes 0 .. TQ/4-1 of one wave fetch 4 lse values
+  // each, the same lanes of the next wave 4 delta values (direct path: the first two waves
+  // of the loading set; register path: waves 0 and 1).  One array per wave keeps each
+  // wave's buffer descriptor uniform.
+  static_assert(HW >= 2, "two waves per loader set");
+  const int rls_w = VEC ? ws : w;            // 0: lse, 1: delta
+  const bool rls_lane = rls_w < 2 && lane < TQ / 4;
   u32x4 rq[VEC ? 1 : NR];
   f32x4 rls = f32x4{0.f, 0.f, 0.f, 0.f};
   auto load_rls = [&](int64_t sr, int jj, bool live) {
     if (rls_lane) {
       const uint32_t lext = live ? (uint32_t)(N - jj * TQ) * 4 : 0u;
-      const uint32_t q0 = 4 * (lane % (TQ / 4));
-      // two uniform descriptors, one per lane half (a per-lane choice of descriptor
-      // would need a loop over its distinct values)
-      const __amdgpu_buffer_rsrc_t rsl = make_rsrc(a.lse + sr, lext);
-      const __amdgpu_buffer_rsrc_t rsd = make_rsrc(a.delta + sr, lext);
+      const uint32_t q0 = 4 * lane;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform_ptr((rls_w == 0 ? a.lse : a.delta) + sr), lext);
       if (LD == 16) {     // rows of lse / delta 16-byte aligned (N % 4 == 0)
-        if (lane < TQ / 4) rls = __builtin_bit_cast(f32x4, buf_ld16(rsl, q0 * 4));
-        else rls = __builtin_bit_cast(f32x4, buf_ld16(rsd, q0 * 4));
+        rls = __builtin_bit_cast(f32x4, buf_ld16(rs, q0 * 4));
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (lane < TQ / 4) rls[i] = __uint_as_float(buf_ld4(rsl, (q0 + i) * 4));
-          else rls[i] = __uint_as_float(buf_ld4(rsd, (q0 + i) * 4));
-        }
+        for (int i = 0; i < 4; ++i) rls[i] = __uint_as_float(buf_ld4(rs, (q0 + i) * 4));
       }
     }
   };
   auto write_rls = [&](int buf) {
     if (rls_lane) {
-      const int q0 = 4 * (lane % (TQ / 4));
-      if (lane >= TQ / 4) *reinterpret_cast<f32x4*>(&sDl[buf][q0]) = -rls;
-      else *reinterpret_cast<f32x4*>(&sL[buf][q0]) = rls * (-1.0f / scale);
+      const int q0 = 4 * lane;
+      if (rls_w == 0) *reinterpret_cast<f32x4*>(&sL[buf][q0]) = rls * (-1.0f / scale);
+      else *reinterpret_cast<f32x4*>(&sDl[buf][q0]) = -rls;
     }
   };
   auto load_stage_direct = [&](int jj, int gg, int buf) {

@@ -75,6 +75,15 @@ template <> struct DOp<16> {
 
 // Raw buffer access: 32-bit byte offsets from a uniform base; reads past
 // `bytes` return zero, which gives free zero fill for ragged tails.
+// A pointer that is the same in every lane, moved to scalar registers (the buffer
+// descriptors built from it are then uniform without a per-value loop).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t x = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return (const T*)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
