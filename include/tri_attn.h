@@ -113,10 +113,10 @@ tri_attn_status tri_attn_bwd_delta(const tri_attn_dims* d, const tri_bf16* o,
  *     tile, evaluating S, P, dP and dS once; one dQ partial per key tile, one dbias
  *     partial per outer group.
  *   D = 32: two kernels.  The key-tile kernel forms dK and dV only; a query-tile kernel
- *     then evaluates S, P, dP and dS again per (32 queries, range of up to 768 keys,
+ *     then evaluates S, P, dP and dS again per (32 queries, range of up to 384 keys,
  *     outer group of up to N_o / L slices), sums each slice's dQ over the key range and
  *     the dbias of its (query, key) block over the whole outer group inside the workgroup:
- *     J_K = ceil(N / 768) dQ partials and L <= 64 dbias partials (L = 8 at N = 768), a
+ *     J_K = ceil(N / 384) dQ partials and L <= 64 dbias partials (L = 8 at N = 768), a
  *     small fraction of the single-pass kernel's partial bytes.
  * Either way every sum has a fixed order, so results are bitwise reproducible.
  */
@@ -224,7 +224,7 @@ int64_t tri_attn_noalloc_scratch_bytes(void);
  * of dQ partials J_K and of dbias partials L, and the key-tile / outer-group sizes behind
  * them.  D = 16, 64 (single-pass kernel): key tile 128; group G = 6 for D = 16 with N
  * even, 4 with N odd, 2 for D = 64.  D = 32 (two kernels): the key range of the
- * query-tile kernel (128, 256, 384, 512 or 768 keys; J_K = ceil(N / 768) ranges) and its
+ * query-tile kernel (128, 256 or 384 keys; J_K = ceil(N / 384) ranges) and its
  * outer group (L <= 64 groups).  Any output pointer may be NULL.  Host-only arithmetic;
  * no device access.
  */

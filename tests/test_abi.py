@@ -163,15 +163,15 @@ def test_workspace_ragged():
             assert api.workspace(d) == ws
 
 
-@pytest.mark.parametrize("B,N_o,H,N,kr,J", [(1, 768, 4, 768, 768, 1), (1, 384, 4, 384, 384, 1),
-                                            (1, 1024, 4, 1024, 512, 2), (2, 5, 2, 100, 128, 1),
-                                            (1, 3, 1, 300, 384, 1), (1, 2, 1, 500, 512, 1),
-                                            (1, 2, 1, 800, 512, 2), (1, 1, 1, 1, 128, 1),
-                                            (1, 70, 1, 40, 128, 1), (1, 9, 3, 2000, 768, 3)])
+@pytest.mark.parametrize("B,N_o,H,N,kr,J", [(1, 768, 4, 768, 384, 2), (1, 384, 4, 384, 384, 1),
+                                            (1, 1024, 4, 1024, 384, 3), (2, 5, 2, 100, 128, 1),
+                                            (1, 3, 1, 300, 384, 1), (1, 2, 1, 500, 256, 2),
+                                            (1, 2, 1, 800, 384, 3), (1, 1, 1, 1, 128, 1),
+                                            (1, 70, 1, 40, 128, 1), (1, 9, 3, 2000, 384, 6)])
 def test_workspace_two_kernel_plan(B, N_o, H, N, kr, J):
-    """D = 32: the query-tile kernel's plan.  J = ceil(N / 768) key ranges of the smallest range
-    (128, 256, 384, 512 or 768 keys) that covers N / J, one FP32 dQ partial per range and one FP32
-    dbias partial per outer group, at most 64 groups of equal size (the last one ragged)."""
+    """D = 32: the query-tile kernel's plan.  J = ceil(N / 384) key ranges of the smallest range
+    (128, 256 or 384 keys) that covers N / J, one FP32 dQ partial per range and one FP32 dbias
+    partial per outer group, at most 64 groups of equal size (the last one ragged)."""
     from triangular_attention_amd import api
     ws = api.workspace(_dims(B=B, N_o=N_o, H=H, N=N, D=32))
     assert ws["key_tile"] == kr and ws["j_k"] == J and J * kr >= N

@@ -43,8 +43,9 @@ CASES = [
     (4, 200, 1, 64, 0.0, 1.0, 1),      # D = 64, 2 key tiles, 7 query tiles of 32 (stage cycle wraps)
     (7, 33, 2, 64, 0.2, 1.0, 2),       # D = 64, odd N (register path), B = 2
     (3, 130, 2, 64, 0.0, 1.0, 1),      # D = 64, no mask, N % 8 == 2, ragged key tile
-    # D = 32, the query-tile kernel's plans: 384-key range (4 waves x 96 keys), 512 (8 x 64),
-    # 768 (8 x 96, the last wave half empty), two key ranges, and more slices than 64 groups
+    # D = 32, the query-tile kernel's plans: one 384-key range (4 waves x 96 keys, the last
+    # wave mostly empty), two 256-key ranges, two and three 384-key ranges, and more slices
+    # than 64 groups
     (2, 300, 1, 32, 0.1, 1.0, 1),
     (2, 504, 1, 32, 0.2, 1.0, 1),
     (2, 700, 1, 32, 0.1, 2.0, 1),

@@ -188,7 +188,8 @@ __global__ __launch_bounds__(TK * 4, TK == 64 ? 3 : 1) void bwd_kernel(BwdArgs a
   uint32_t qoff[NQPW];                      // wave ws loads pieces ws, ws + HW, ..
 #pragma unroll
   for (int k = 0; k < NQPW; ++k) {
-    const int slot = (ws + k * HW) * 64 + lane, row = slot / SPR, ch = Lay<D>::q_src_chunk(row, slot % SPR);
+    const int slot = (ws + k * HW) * 64 + lane, row = Lay<D>::q_src_row(slot / SPR);
+    const int ch = Lay<D>::q_src_chunk(row, slot % SPR);
     qoff[k] = (uint32_t)(row * D + ch * 8) * 2;
   }
   // -lse/scale and -delta of a stage: lanes 0 .. TQ/4-1 of one wave fetch 4 lse values

@@ -7,23 +7,29 @@
 
 namespace tri {
 
-// Element offset of (row, col) in the LDS tiles.  D = 32: unpadded rows, chunk
-// XOR swizzle: Q/dO by row bits 3-4, K by row bits 2-3.  D = 16: rows padded
-// to 24 elements.
+// Element offset of (row, col) in the LDS tiles.  D = 32: unpadded 64-byte rows.  Q, dO
+// (and V): row r at row position pq(r) (row bit 4 copied into bit 2), its 16-byte chunks
+// XORed with 2 where row bit 3 is set, so that the score-product reads (rows
+// 8(c/4) + 4e + c%4 of a 32-row tile, one chunk per lane group), the transposing reads and
+// 16 consecutive rows all touch distinct banks per half-wave; K: chunk XOR by row bits 2-3.
+// D = 16: Q / dO rows padded to 24 elements.
 template <int D> struct Lay;
 template <> struct Lay<32> {
   static constexpr int kRowElems = 32;
   static constexpr int kKVRowElems = 32;
-  __device__ static __forceinline__ int swq(int row) { return ((row >> 3) & 1) << 1 | ((row >> 4) & 1); }
+  __device__ static __forceinline__ int pq(int row) { return row ^ (((row >> 4) & 1) << 2); }
+  __device__ static __forceinline__ int swq(int row) { return ((row >> 3) & 1) << 1; }
   __device__ static __forceinline__ int swk(int row) { return (row >> 2) & 3; }
   __device__ static __forceinline__ int q(int row, int col) {
-    return row * 32 + ((((col >> 3) ^ swq(row)) & 3) << 3) + (col & 7);
+    return pq(row) * 32 + ((((col >> 3) ^ swq(row)) & 3) << 3) + (col & 7);
   }
   __device__ static __forceinline__ int k(int row, int col) {
     return row * 32 + ((((col >> 3) ^ swk(row)) & 3) << 3) + (col & 7);
   }
   __device__ static __forceinline__ int v(int row, int col) { return q(row, col); }
-  // logical chunk stored in physical slot `pchunk` of `row`
+  // logical row stored at row position `prow` (pq is an involution), and the logical chunk
+  // stored in physical slot `pchunk` of logical row `row`
+  __device__ static __forceinline__ int q_src_row(int prow) { return pq(prow); }
   __device__ static __forceinline__ int q_src_chunk(int row, int pchunk) { return (pchunk ^ swq(row)) & 3; }
   static constexpr int kSlotsPerRow = 4;
 };
@@ -41,6 +47,7 @@ template <> struct Lay<16> {
     return (row ^ (hi << 2)) * 16 + ((((col >> 2) ^ (hi << 1)) & 3) << 2) + (col & 3);
   }
   __device__ static __forceinline__ int v(int row, int col) { return k(row, col); }
+  __device__ static __forceinline__ int q_src_row(int prow) { return prow; }
   __device__ static __forceinline__ int q_src_chunk(int row, int pchunk) { return pchunk < 2 ? pchunk : 0; }
   static constexpr int kSlotsPerRow = 3;     // two data chunks and one padding chunk
 };
@@ -67,6 +74,7 @@ template <> struct Lay<64> {
     return row * 64 + ((((col >> 3) ^ swk(row)) & 7) << 3) + (col & 7);
   }
   __device__ static __forceinline__ int v(int row, int col) { return k(row, col); }
+  __device__ static __forceinline__ int q_src_row(int prow) { return prow; }
   __device__ static __forceinline__ int q_src_chunk(int row, int pchunk) { return (pchunk ^ swq(row)) & 7; }
   static constexpr int kSlotsPerRow = 8;
 };

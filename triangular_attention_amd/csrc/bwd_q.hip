@@ -7,12 +7,12 @@
 //
 // Work split.  The key-tile kernel (bwd.hip, dK/dV-only variant) forms dK and dV; this
 // kernel forms dQ and dbias and evaluates S, P, dP and dS a second time.  A workgroup owns
-// 32 queries of one head, one range of up to 768 keys and one outer group of consecutive
+// 32 queries of one head, one range of up to 384 keys and one outer group of consecutive
 // slices, which it visits in ascending order, so that
 //  - dbias of its (query, key) block is summed over the whole group in FP32 registers and
 //    written once per group: L = a few groups instead of N_o / 4, and
 //  - each slice's dQ over the key range is summed inside the workgroup: one FP32 dQ
-//    partial per key range (a single one for N <= 768) instead of one per 128 keys.
+//    partial per key range (two for N = 768) instead of one per 128 keys.
 // The partials of the single-pass design (TurboPairFormer, Figure 7(c)-(d)) cost
 // 4 (J_K X + L Y) bytes written and read again; at N = 768, D = 32 that round trip is
 // 7.2 GB, more than twice the time of this second evaluation of the scores.
@@ -46,7 +46,7 @@ namespace {
 // Byte offset, relative to the tile's first row, of the 16 bytes that a direct load stores
 // in physical 16-byte slot `slot` of a Q (or dO) tile in the Lay<32>::q layout ...
 __device__ __forceinline__ uint32_t q_src(int slot) {
-  const int row = slot >> 2;
+  const int row = Lay<32>::q_src_row(slot >> 2);
   return (uint32_t)(row * 32 + Lay<32>::q_src_chunk(row, slot & 3) * 8) * 2;
 }
 // ... and of a K tile in the Lay<32>::k layout (16-byte chunk XORed with row bits 2-3)
@@ -338,8 +338,6 @@ static hipError_t launch_bwdq_d(const BwdQArgs& a, hipStream_t s) {
   if (nw == 4 && np == 1) return launch_bwdq_t<D, MASK, 4, 1>(a, s);
   if (nw == 4 && np == 2) return launch_bwdq_t<D, MASK, 4, 2>(a, s);
   if (nw == 4 && np == 3) return launch_bwdq_t<D, MASK, 4, 3>(a, s);
-  if (nw == 8 && np == 2) return launch_bwdq_t<D, MASK, 8, 2>(a, s);
-  if (nw == 8 && np == 3) return launch_bwdq_t<D, MASK, 8, 3>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -103,7 +103,10 @@ struct SegReduceArgs {
 // (query, key) block accumulates over the group in FP32 registers (one partial per group),
 // and each slice's dQ over the range is complete in the workgroup (one partial per range).
 constexpr int kBwdQQueries = 32;
-constexpr int kBwdQMaxRange = 768;
+// At most 384 keys per range (4 waves x 96 keys): two such workgroups (79 KB of LDS each) share
+// a CU and their per-slice barriers fall at independent times; one 8-wave workgroup over 768
+// keys (152 KB) measured 4% slower at N = 768 even with its single dQ partial.
+constexpr int kBwdQMaxRange = 384;
 constexpr int kDeviceCUs = 256;          // MI355X compute units
 struct BwdQPlan {
   int nw, np;         // waves per workgroup, 32-key pairs per wave
@@ -115,17 +118,17 @@ inline BwdQPlan bwdq_plan(int64_t B, int64_t N_o, int64_t H, int64_t N) {
   BwdQPlan p;
   p.n_ranges = (int)((N + kBwdQMaxRange - 1) / kBwdQMaxRange);
   const int64_t need = (N + p.n_ranges - 1) / p.n_ranges;
-  // smallest range that holds `need` keys: 128 (4 x 1), 256 (4 x 2), 384 (4 x 3), 512 (8 x 2), 768 (8 x 3)
-  static const int opt[5][2] = {{4, 1}, {4, 2}, {4, 3}, {8, 2}, {8, 3}};
+  // smallest range that holds `need` keys: 128 (4 x 1), 256 (4 x 2), 384 (4 x 3)
+  static const int opt[3][2] = {{4, 1}, {4, 2}, {4, 3}};
   int i = 0;
-  while (i < 4 && 32 * opt[i][0] * opt[i][1] < need) ++i;
+  while (i < 2 && 32 * opt[i][0] * opt[i][1] < need) ++i;
   p.nw = opt[i][0];
   p.np = opt[i][1];
   p.kr = 32 * p.nw * p.np;
   p.n_qt = (int)((N + kBwdQQueries - 1) / kBwdQQueries);
   // outer groups: fewest rounds of workgroups x slices per workgroup (plus a per-workgroup
-  // start-up of about 1.5 slices); workgroups per CU: 1 with 8 waves, 2 with 4
-  const int64_t slots = (int64_t)kDeviceCUs * (p.nw == 8 ? 1 : 2);
+  // start-up of about 1.5 slices); two workgroups per CU
+  const int64_t slots = (int64_t)kDeviceCUs * 2;
   const int64_t units = B * H * p.n_ranges * p.n_qt;
   double best = 0;
   int bestL = 1;
