@@ -90,8 +90,7 @@ __global__ __launch_bounds__(TK * 4, TK == 64 ? 3 : 1) void bwd_kernel(BwdArgs a
 
   __shared__ __align__(16) uint16_t sQ[NB][TQ * RE];
   __shared__ __align__(16) uint16_t sdO[NB][TQ * RE];
-  __shared__ __align__(16) float sL[NB][TQ];    // -lse / scale of the stage's rows
-  __shared__ __align__(16) float sDl[NB][TQ];   // -delta
+  __shared__ __align__(16) float sLD[2][NB][TQ];   // -lse / scale (0) and -delta (1) of the stage's rows
   __shared__ __align__(16) uint16_t sdS[KV ? 1 : 2][KV ? 8 : TK * SP];
   __shared__ __align__(16) uint16_t sK[G][TK * KRE];
   __shared__ __align__(16) uint16_t sV[G][TK * KRE];   // V rows of the key tile (row-read layout)
@@ -214,12 +213,9 @@ __global__ __launch_bounds__(TK * 4, TK == 64 ? 3 : 1) void bwd_kernel(BwdArgs a
       }
     }
   };
+  const float rls_f = rls_w == 0 ? -1.0f / scale : -1.0f;
   auto write_rls = [&](int buf) {
-    if (rls_lane) {
-      const int q0 = 4 * lane;
-      if (rls_w == 0) *reinterpret_cast<f32x4*>(&sL[buf][q0]) = rls * (-1.0f / scale);
-      else *reinterpret_cast<f32x4*>(&sDl[buf][q0]) = -rls;
-    }
+    if (rls_lane) *reinterpret_cast<f32x4*>(&sLD[rls_w & 1][buf][4 * lane]) = rls * rls_f;
   };
   auto load_stage_direct = [&](int jj, int gg, int buf) {
     const int64_t sr = srow(gg) + (int64_t)jj * TQ;     // first row of the tile
@@ -456,14 +452,17 @@ __global__ __launch_bounds__(TK * 4, TK == 64 ? 3 : 1) void bwd_kernel(BwdArgs a
   auto query_tile = [&](int j, auto full_c, auto r0_c) {
     constexpr bool FULL = decltype(full_c)::value;
     constexpr int R0 = decltype(r0_c)::value;
-    // bias * log2(e) of the lane's (query, key) pairs: one transposing read per block
-    // gives rows 32s + 8g + 4e + 0..3 of block qb = 2s + e at the lane's key column
+    // bias of the lane's (query, key) pairs: one transposing read per block gives rows
+    // 32s + 8g + 4e + 0..3 of block qb = 2s + e at the lane's key column.  Without a mask
+    // it is kept as bias * log2(e); with one as the bias itself, and each stage forms
+    // bias * log2(e) + mask * log2(e) in one FMA (for a zero mask the same value)
     f32x4 bb[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int r0 = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);
       const u32x2 bw = ds_read_tr(&sB[j & 1][b_at(r0 + trk, 16 * w + 4 * tra)]);
-      bb[qb] = f32x4{bf_lo(bw[0]), bf_hi(bw[0]), bf_lo(bw[1]), bf_hi(bw[1])} * kLog2e;
+      bb[qb] = f32x4{bf_lo(bw[0]), bf_hi(bw[0]), bf_lo(bw[1]), bf_hi(bw[1])};
+      if constexpr (!MASK) bb[qb] *= kLog2e;
     }
     f32x4 dbacc[NQB];       // sum over the group's slices of the FP32 dS, in slice order
     // this group's dbias partial of query tile j (the FP32 sum over the group's slices)
@@ -532,15 +531,15 @@ __global__ __launch_bounds__(TK * 4, TK == 64 ? 3 : 1) void bwd_kernel(BwdArgs a
           const int r0 = 32 * st + 8 * g + 4 * e;
           const QT qa = ld_op<D>(tq, ql, g * QL, lq);
           const QT da = ld_op<D>(tdo, ql, g * QL, lq);
-          const f32x4 nl = *reinterpret_cast<const f32x4*>(&sL[buf][r0]);
-          const f32x4 nd = *reinterpret_cast<const f32x4*>(&sDl[buf][r0]);
+          const f32x4 nl = *reinterpret_cast<const f32x4*>(&sLD[0][buf][r0]);
+          const f32x4 nd = *reinterpret_cast<const f32x4*>(&sLD[1][buf][r0]);
           const f32x4 sv = DOp<D>::mma(qa, kb, nl);        // q.k - lse/scale
           const f32x4 dp = DOp<D>::mma(da, vb, nd);        // dP - delta
           float p[4], ds[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float x = fmaf(sv[i], c1, bb[qb][i]);
-            if (MASK) x += mk2[gs];
+            const float bm = MASK ? fmaf(bb[qb][i], kLog2e, mk2[gs]) : bb[qb][i];
+            const float x = fmaf(sv[i], c1, bm);
             p[i] = __builtin_amdgcn_exp2f(x);
             ds[i] = p[i] * dp[i];
           }
