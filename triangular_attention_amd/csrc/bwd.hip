@@ -79,6 +79,7 @@ __global__ __launch_bounds__(TK * 4, TK == 64 ? 3 : 1) void bwd_kernel(BwdArgs a
   constexpr int CH = D / 8;       // 16-byte chunks per row in memory
   constexpr int NDB = D / 16;
   constexpr int NQCH = TQ * CH;   // chunks of one Q (or dO) tile
+  static_assert(NQCH % 64 == 0, "a wave's register-path chunks lie in one of Q, dO");
   constexpr int NBCH = TQ * TK / 8;   // 16-byte chunks of one bias tile
   constexpr int NR = (2 * NQCH + NT - 1) / NT;
   constexpr int NRB = (NBCH + NT - 1) / NT;
@@ -241,7 +242,9 @@ __global__ __launch_bounds__(TK * 4, TK == 64 ? 3 : 1) void bwd_kernel(BwdArgs a
     for (int r = 0; r < NR; ++r) {
       const int ci = tid + r * NT;
       if (ci < 2 * NQCH) {
-        const int which = ci / NQCH, cc = ci % NQCH;
+        // Q or dO: the same for the whole wave (NQCH is a multiple of 64), so the choice of
+        // descriptor stays uniform
+        const int which = __builtin_amdgcn_readfirstlane(ci / NQCH), cc = ci % NQCH;
         const int row = cc / CH, ch = cc % CH;
         rq[r] = buf_ld16(which ? rO : rQ, (uint32_t)(row * D + ch * 8) * 2);
       }
