@@ -297,6 +297,32 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
     }
   };
 
+  // D = 16, 32 with every tile in LDS: the lane's byte offsets of its tile reads, formed once.
+  // Within a read kind the other reads differ from these by compile-time amounts (m: +32
+  // rows; qb: +16 bias rows; e of the mask: +4 floats), so each read is one of these
+  // registers plus the instruction's offset field; without them the compiler forms the
+  // swizzled addresses again in every tile.
+  constexpr bool HOIST = D != 64 && LDSIN;
+  uint32_t rbo[2] = {0u, 0u}, kao[2] = {0u, 0u}, vao[2][NDB], rmo = 0u;
+  if constexpr (HOIST) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) rbo[m] = (uint32_t)((32 * w + c) * TK + (((4 * m + g) ^ swb(c)) * 8)) * 2;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) kao[e] = (uint32_t)kv_at(8 * (c >> 2) + 4 * e + (c & 3), g * QL) * 2;
+    const int k = (lane & 15) >> 2;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vao[hi][db] = (uint32_t)kv_at(8 * g + k + 4 * hi, 16 * db + 4 * (lane & 3)) * 2;
+    rmo = (uint32_t)(8 * g) * 4;
+    asm volatile("" : "+v"(rbo[0]), "+v"(rbo[1]), "+v"(kao[0]), "+v"(kao[1]), "+v"(rmo));
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(vao[hi][db]));
+  }
+  auto at = [](const void* base, uint32_t off) { return (const uint16_t*)((const char*)base + off); };
+
   float mref[2] = {-INFINITY, -INFINITY};   // reference maximum (natural units)
   float lsum[2] = {0.f, 0.f};               // this lane's part of the row sum, relative to mref
   f32x4 oacc[NDB][2];
@@ -314,7 +340,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
     uint16_t* const tV = BUF ? sV1 : sV0;
     float* const tM = BUF ? sM1 : sM0;
     uint16_t* const tB = BUF ? sB1 : sB0;
-    if constexpr (LDSIN) {
+    if constexpr (HOIST) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) rb[qb][m] = ld_shared<u32x4>(at(tB + 16 * qb * TK, rbo[m]));
+    } else if constexpr (LDSIN) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -327,7 +358,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) rm[m][e] = *reinterpret_cast<const f32x4*>(&tM[32 * m + 8 * g + 4 * e]);
+        for (int e = 0; e < 2; ++e) {
+          if constexpr (HOIST) rm[m][e] = *reinterpret_cast<const f32x4*>(at(tM + 32 * m + 4 * e, rmo));
+          else rm[m][e] = *reinterpret_cast<const f32x4*>(&tM[32 * m + 8 * g + 4 * e]);
+        }
     }
 
     // S^T blocks: rows = keys 32m + 8(r/4) + 4e + (r%4), so that lane group g
@@ -355,6 +389,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
         if constexpr (D == 64) {       // two chunks, each at its own swizzled position
           ka[m][e].x[0] = ld_shared<u32x4>(&tK[kv_at(kl, 8 * kc)]);
           ka[m][e].x[1] = ld_shared<u32x4>(&tK[kv_at(kl, 8 * kc + 8)]);
+        } else if constexpr (HOIST) {
+          ka[m][e] = ld_shared<QT>(at(tK + 32 * m * KP, kao[e]));
         } else {
           ka[m][e] = ld_shared<QT>(&tK[kv_at(kl, g * QL)]);
         }
@@ -407,9 +443,15 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         // lane (k, a) of its group: rows r0 + k and r0 + 4 + k, columns 16 db + 4a .. +3
-        const int k = (lane & 15) >> 2, a4 = 16 * db + 4 * (lane & 3);
-        const int r0 = 32 * m + 8 * g + k, r1 = r0 + 4;
-        va[m][db] = ds_read_tr8_at(tV, kv_at(r0, a4), kv_at(r1, a4));
+        if constexpr (HOIST) {
+          const u32x2 lo = ds_read_tr(at(tV + 32 * m * KP, vao[0][db]));
+          const u32x2 hi = ds_read_tr(at(tV + 32 * m * KP, vao[1][db]));
+          va[m][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          const int k = (lane & 15) >> 2, a4 = 16 * db + 4 * (lane & 3);
+          const int r0 = 32 * m + 8 * g + k, r1 = r0 + 4;
+          va[m][db] = ds_read_tr8_at(tV, kv_at(r0, a4), kv_at(r1, a4));
+        }
       }
 
 #pragma unroll
