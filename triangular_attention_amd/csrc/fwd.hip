@@ -148,6 +148,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
 
   const int nkt = (N + TK - 1) / TK;
   const bool ragged = (N % TK) != 0;
+  // a power-of-two scale (D = 16, 64 with the usual 1/sqrt(D)) makes every lo term exactly
+  // zero: its products are skipped (D = 32, 64; D = 16 folds both terms into one product)
+  const bool need_lo = (__float_as_uint(a.scale) & 0x7FFFFFu) != 0u;
 
   // Direct global->LDS loads of a tile, in whole-wave pieces (lane l of a piece fills
   // 16-byte slot l).  K and V tiles are unpadded, with row r stored at row position pr(r)
@@ -408,12 +411,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 3) void fwd_kernel(FwdArgs a) {
             sacc[qb][m][e] = mfma_k32(kk, u32x4{qhi[qb][0], qhi[qb][1], qlo[qb][0], qlo[qb][1]}, sacc[qb][m][e]);
         }
     } else {
+      if (need_lo) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
+          for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) sacc[qb][m][e] = DOp<D>::mma(ka[m][e], qlo[qb], sacc[qb][m][e]);
+            for (int qb = 0; qb < 2; ++qb) sacc[qb][m][e] = DOp<D>::mma(ka[m][e], qlo[qb], sacc[qb][m][e]);
+      }
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
