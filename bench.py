@@ -361,8 +361,9 @@ def bench_attn(args, w, dev):
     d = ta.dims_of(q, w.scale)
     bp = args.partials == "bf16"
     ws = ta.workspace(d, single_pass=bp)
-    # the default FP32 backward call runs two kernels for D = 32 (dK/dV, then dQ/dbias)
-    two = w.D == 32 and not bp
+    # the default FP32 backward call runs two kernels (dK/dV, then dQ/dbias) for D = 32 and
+    # for D = 16 past N = 640
+    two = (w.D == 32 or (w.D == 16 and w.N > 640)) and not bp
     comp = not args.no_compensate
     o = torch.empty_like(q)
     o_res = torch.empty_like(q) if comp else None

@@ -148,7 +148,8 @@ def test_workspace_ragged():
     """Partial counts of the single-pass key-tile kernel for ragged shapes.  The outer group is
     4 slices except on the direct-load path with D = 16 (N even), where the smaller accumulators
     leave room for 6, and 2 slices for D = 64, whose accumulators are twice as large.  For
-    D = 16 and 64 the default backward is that kernel, so both queries agree."""
+    D = 64, and D = 16 up to N = 640, the default backward is that kernel, so both queries
+    agree."""
     from triangular_attention_amd import api
     for (N_o, N, D, G) in ((10, 65, 16, 4), (10, 64, 16, 6), (10, 66, 16, 6), (10, 64, 32, 4), (13, 200, 16, 6),
                            (13, 201, 32, 4), (13, 200, 64, 2), (13, 201, 64, 2)):
@@ -159,7 +160,7 @@ def test_workspace_ragged():
         assert ws["j_k"] == jk and ws["l"] == L
         assert ws["dq_partial_elems"] == jk * 2 * N_o * 3 * N * D
         assert ws["dbias_partial_elems"] == L * 2 * 3 * N * N
-        if D != 32:
+        if D != 32:     # N <= 640: D = 16 runs the single-pass kernel too
             assert api.workspace(d) == ws
 
 
@@ -169,16 +170,17 @@ def test_workspace_ragged():
                                             (1, 2, 1, 800, 384, 3), (1, 1, 1, 1, 128, 1),
                                             (1, 70, 1, 40, 128, 1), (1, 9, 3, 2000, 384, 6)])
 def test_workspace_two_kernel_plan(B, N_o, H, N, kr, J):
-    """D = 32: the query-tile kernel's plan.  J = ceil(N / 384) key ranges of the smallest range
+    """D = 32 (and D = 16 past N = 640): the query-tile kernel's plan.  J = ceil(N / 384) key ranges of the smallest range
     (128, 256 or 384 keys) that covers N / J, one FP32 dQ partial per range and one FP32 dbias
     partial per outer group, at most 64 groups of equal size (the last one ragged)."""
     from triangular_attention_amd import api
-    ws = api.workspace(_dims(B=B, N_o=N_o, H=H, N=N, D=32))
-    assert ws["key_tile"] == kr and ws["j_k"] == J and J * kr >= N
-    gs, L = ws["outer_group"], ws["l"]
-    assert 1 <= L <= min(64, N_o) and L == -(-N_o // gs) and (L - 1) * gs < N_o
-    assert ws["dq_partial_elems"] == J * B * N_o * H * N * 32
-    assert ws["dbias_partial_elems"] == L * B * H * N * N
+    for D in ((16, 32) if N > 640 else (32,)):
+        ws = api.workspace(_dims(B=B, N_o=N_o, H=H, N=N, D=D))
+        assert ws["key_tile"] == kr and ws["j_k"] == J and J * kr >= N
+        gs, L = ws["outer_group"], ws["l"]
+        assert 1 <= L <= min(64, N_o) and L == -(-N_o // gs) and (L - 1) * gs < N_o
+        assert ws["dq_partial_elems"] == J * B * N_o * H * N * D
+        assert ws["dbias_partial_elems"] == L * B * H * N * N
 
 
 # --------------------------------------------------------------------------- block ABI

@@ -1,8 +1,8 @@
 """The chunked backward (tri_attn_bwd_chunked; TurboPairFormer, Figure 7(d) and Table 2:
 partial buffers reused once consumed, so only one chunk of outer groups has partials at a
 time) runs the single-pass key-tile kernel.  For every chunk size it is bitwise equal to the
-same kernel run as one chunk (all outer groups) and, for D = 16 and 64, whose default
-backward is that kernel, to the three unchunked calls; including ragged last chunks, ragged
+same kernel run as one chunk (all outer groups) and, where the default backward is that kernel
+(D = 64; D = 16 up to N = 640), to the three unchunked calls; including ragged last chunks, ragged
 last outer groups, B > 1, odd N (scalar reduction path), D = 16 (outer group 6) and D = 64
 (outer group 2); and at full size, where it is also checked against the oracle on sampled
 outputs.
@@ -26,10 +26,12 @@ def _bits(t):
 
 def _both(ta, dev, scale, chunk_groups):
     """The chunked backward at each chunk size, and its reference: the same kernel as one chunk
-    (D = 32), or the three unchunked calls (D = 16, 64: the same kernel)."""
+    where the default backward runs two kernels (D = 32; D = 16 past N = 640), else the three
+    unchunked calls (the same kernel)."""
     o, o_res, lse = ta.forward(dev["q"], dev["k"], dev["v"], dev["bias"], dev["mask"], scale)
     args = (dev["q"], dev["k"], dev["v"], dev["bias"], dev["mask"], scale, o, o_res, lse, dev["do"])
-    if dev["q"].shape[-1] == 32:
+    D, N = dev["q"].shape[-1], dev["q"].shape[-2]
+    if D == 32 or (D == 16 and N > 640):
         ref = ta.backward_chunked(*args)          # one chunk of all outer groups
     else:
         ref = ta.backward(*args)

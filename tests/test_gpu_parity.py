@@ -51,6 +51,11 @@ CASES = [
     (2, 700, 1, 32, 0.1, 2.0, 1),
     (1, 800, 1, 32, 0.1, 1.0, 1),
     (70, 40, 1, 32, 0.1, 1.0, 1),
+    # D = 16 past N = 640 (two kernels): 16-byte loads (64-key dK/dV tiles), 4-byte loads and
+    # odd N (128-key dK/dV tiles, direct and register-staged), two and three key ranges
+    (2, 656, 1, 16, 0.1, 1.0, 1),
+    (2, 650, 1, 16, 0.2, 2.0, 1),
+    (3, 771, 1, 16, 0.1, 1.0, 1),
 ]
 
 

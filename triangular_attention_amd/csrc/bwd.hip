@@ -64,7 +64,9 @@ __global__ __launch_bounds__(TK * 4, TK == 64 ? 3 : 1) void bwd_kernel(BwdArgs a
   constexpr bool VEC = LD != 0;   // direct global->LDS path
   constexpr int NW = TK / 16;     // waves; wave w owns keys 16w..16w+15 of the tile
   constexpr int NT = NW * 64;
-  constexpr int TQ = TK == 64 ? 32 : bwd_query_tile(D), G = TK == 64 ? 2 : bwd_group(D, VEC);
+  // 64-key tiles (dK/dV only): 32-query stages, 64 for D = 16 (its padded 48-byte Q rows
+  // make whole-wave pieces only in 64-row tiles)
+  constexpr int TQ = TK == 64 ? (D == 16 ? 64 : 32) : bwd_query_tile(D), G = TK == 64 ? 2 : bwd_group(D, VEC);
   constexpr int NQB = TQ / 16;    // 16-query blocks of a stage
   constexpr int NST = TQ / 32;    // 32-query halves of a stage (dV / dK contraction steps)
   static_assert(TQ % 32 == 0, "query tile must be whole 32-query halves");
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(TK * 4, TK == 64 ? 3 : 1) void bwd_kernel(BwdArgs a
   constexpr int NRB = (NBCH + NT - 1) / NT;
   constexpr int NBLK = NQB * NDB; // dQ output blocks per stage
   static_assert(KV || NBLK <= NW, "one dQ block per wave at most");
-  static_assert(TK == 128 || (TK == 64 && KV && LD == 16 && D == 32), "64-key tiles: dK/dV only, D = 32, 16-byte loads");
+  static_assert(TK == 128 || (TK == 64 && KV && LD == 16 && D != 64), "64-key tiles: dK/dV only, D = 16, 32, 16-byte loads");
   typedef typename DOp<D>::T QT;
   constexpr int QL = DOp<D>::kPerLane;
 
@@ -653,8 +655,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int64_t nunit = (int64_t)a.B * a.n_groups * a.H;
   const int64_t nblk = 8 * ((nunit + 7) / 8) * a.n_key_tiles;
   if (a.kv_only) {
-    // dK / dV only (the two-kernel backward, D = 32)
-    if constexpr (D != 32) {
+    // dK / dV only (the two-kernel backward, D = 16 and 32)
+    if constexpr (D == 64) {
       return hipErrorInvalidValue;
     } else if constexpr (LD == 16) {
       // 64-key tiles over outer groups of 2 slices

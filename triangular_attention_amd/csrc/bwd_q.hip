@@ -43,16 +43,33 @@ namespace tri {
 
 namespace {
 
-// Byte offset, relative to the tile's first row, of the 16 bytes that a direct load stores
-// in physical 16-byte slot `slot` of a Q (or dO) tile in the Lay<32>::q layout ...
-__device__ __forceinline__ uint32_t q_src(int slot) {
-  const int row = Lay<32>::q_src_row(slot >> 2);
-  return (uint32_t)(row * 32 + Lay<32>::q_src_chunk(row, slot & 3) * 8) * 2;
+// Q / dO tile element offset: D = 32 uses the swizzled 64-byte rows of the key-tile kernel,
+// D = 16 plain 32-byte rows (only row reads here).
+template <int D> __device__ __forceinline__ int q_at(int row, int col) {
+  if constexpr (D == 32) return Lay<32>::q(row, col);
+  else return row * 16 + col;
 }
-// ... and of a K tile in the Lay<32>::k layout (16-byte chunk XORed with row bits 2-3)
-__device__ __forceinline__ uint32_t k_src(int slot) {
-  const int row = slot >> 2;
-  return (uint32_t)(row * 32 + ((slot & 3) ^ Lay<32>::swk(row)) * 8) * 2;
+// Byte offset, relative to the tile's first row, of the 16 bytes that a direct load stores
+// in physical 16-byte slot `slot` of a Q (or dO) tile ...
+template <int D> __device__ __forceinline__ uint32_t q_src(int slot) {
+  if constexpr (D == 32) {
+    const int row = Lay<32>::q_src_row(slot >> 2);
+    return (uint32_t)(row * 32 + Lay<32>::q_src_chunk(row, slot & 3) * 8) * 2;
+  } else {
+    return (uint32_t)slot * 16;
+  }
+}
+// ... and of a K tile in the Lay<D>::k layouts (D = 32: 16-byte chunk XORed with row bits
+// 2-3; D = 16: rows 8-11 and 12-15 of each 16-row group trade places and the two chunks of
+// those rows swap)
+template <int D> __device__ __forceinline__ uint32_t k_src(int slot) {
+  if constexpr (D == 32) {
+    const int row = slot >> 2;
+    return (uint32_t)(row * 32 + ((slot & 3) ^ Lay<32>::swk(row)) * 8) * 2;
+  } else {
+    const int prow = slot >> 1, hi = (prow >> 3) & 1;
+    return (uint32_t)((prow ^ (hi << 2)) * 16 + ((slot & 1) ^ hi) * 8) * 2;
+  }
 }
 
 }  // namespace
@@ -71,7 +88,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
   constexpr int MW = KWP <= 64 ? 64 : 128;     // mask floats per wave tile (4-byte loads of 64 lanes)
   constexpr int RP = D + 4;                    // row pitch (floats) of the dQ^T tiles in LDS
   constexpr int RED = TQ * D / 4;              // 16-byte items of one dQ tile
-  static_assert(D == 32, "query-tile backward: D = 32");
+  static_assert(D == 16 || D == 32, "query-tile backward: D = 16 or 32");
   static_assert(KWP * CH % 64 == 0 && TQ * CH % 64 == 0 && NW >= 3 && RED <= NT, "tile shapes");
 
   __shared__ __align__(16) uint16_t sK[2][NW][KWP * D];
@@ -144,7 +161,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
     const u32x4 rk = make_rsrc_words(a.k + sr * D, kv_bytes);
 #pragma unroll
     for (int i = 0; i < KDMA; ++i)
-      dma16(rk, sK[buf][w] + 512 * i, (uint32_t)kw0 * D * 2 + k_src(64 * i + lane));
+      dma16(rk, sK[buf][w] + 512 * i, (uint32_t)kw0 * D * 2 + k_src<D>(64 * i + lane));
     if constexpr (MASK) {
       const u32x4 rm = make_rsrc_words(a.mask + ((int64_t)b * N_o + o) * N, (uint32_t)N * 4);
 #pragma unroll
@@ -154,11 +171,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
     if (w == 0) {
       const u32x4 rq = make_rsrc_words(a.q + (sr + q0) * D, ext);
 #pragma unroll
-      for (int i = 0; i < QDMA; ++i) dma16(rq, sQ[buf] + 512 * i, q_src(64 * i + lane));
+      for (int i = 0; i < QDMA; ++i) dma16(rq, sQ[buf] + 512 * i, q_src<D>(64 * i + lane));
     } else if (w == 1) {
       const u32x4 ro = make_rsrc_words(a.d_o + (sr + q0) * D, ext);
 #pragma unroll
-      for (int i = 0; i < QDMA; ++i) dma16(ro, sdO[buf] + 512 * i, q_src(64 * i + lane));
+      for (int i = 0; i < QDMA; ++i) dma16(ro, sdO[buf] + 512 * i, q_src<D>(64 * i + lane));
     } else if (w == 2) {
       const uint32_t lext = (uint32_t)(N - q0) * 4;
       dma4(make_rsrc_words(a.lse + sr + q0, lext), sLD[buf], (uint32_t)lane * 4);
@@ -172,7 +189,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
     for (int e = 0; e < 2; ++e) {
       const int key = kw0 + 32 * p + 8 * (c >> 2) + 4 * e + (c & 3);
       const uint32_t off = (uint32_t)(key * D + g * QL) * 2;
-      vb[e] = buf_ld16(rv, off);
+      if constexpr (D == 32) vb[e] = buf_ld16(rv, off);
+      else vb[e] = buf_ld8(rv, off);
     }
   };
   // the workgroup's dQ rows of slice o: item tid of the summed tile, stored in the key
@@ -211,7 +229,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
     // the slice's -lse log2(e) and -delta of the lane's queries
     float nl[NQB];
     f32x4 nd[NQB];
-    const auto lq = [](int rr, int cc) { return Lay<32>::q(rr, cc); };
+    const auto lq = [](int rr, int cc) { return q_at<D>(rr, cc); };
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       nl[qb] = -sLD[buf][16 * qb + c] * kLog2e;
@@ -344,6 +362,7 @@ static hipError_t launch_bwdq_d(const BwdQArgs& a, hipStream_t s) {
 hipError_t launch_bwdq(const BwdQArgs& a, int D, hipStream_t s) {
   const bool mask = a.mask != nullptr;
   if (D == 32) return mask ? launch_bwdq_d<32, true>(a, s) : launch_bwdq_d<32, false>(a, s);
+  if (D == 16) return mask ? launch_bwdq_d<16, true>(a, s) : launch_bwdq_d<16, false>(a, s);
   return hipErrorInvalidValue;
 }
 
