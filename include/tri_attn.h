@@ -108,16 +108,17 @@ tri_attn_status tri_attn_bwd_delta(const tri_attn_dims* d, const tri_bf16* o,
  * dQ (already scaled) leaves as J_K FP32 partials and dbias as L FP32 partials, each
  * element written by exactly one workgroup (Figure 11(a), materialised partials), with
  * J_K and L as reported by tri_attn_workspace.
- *   D = 16, 64: the single-pass key-tile kernel (Figure 7(c)): one workgroup owns one
- *     128-key tile of one head for one outer group of G slices and visits every query
- *     tile, evaluating S, P, dP and dS once; one dQ partial per key tile, one dbias
- *     partial per outer group.
- *   D = 32: two kernels.  The key-tile kernel forms dK and dV only; a query-tile kernel
- *     then evaluates S, P, dP and dS again per (32 queries, range of up to 384 keys,
- *     outer group of up to N_o / L slices), sums each slice's dQ over the key range and
- *     the dbias of its (query, key) block over the whole outer group inside the workgroup:
- *     J_K = ceil(N / 384) dQ partials and L <= 64 dbias partials (L = 8 at N = 768), a
- *     small fraction of the single-pass kernel's partial bytes.
+ *   D = 64, and D = 16 with N <= 640: the single-pass key-tile kernel (Figure 7(c)):
+ *     one workgroup owns one 128-key tile of one head for one outer group of G slices
+ *     and visits every query tile, evaluating S, P, dP and dS once; one dQ partial per
+ *     key tile, one dbias partial per outer group.
+ *   D = 32, and D = 16 with N > 640: two kernels.  The key-tile kernel forms dK and dV
+ *     only; a query-tile kernel then evaluates S, P, dP and dS again per (32 queries,
+ *     range of up to 384 keys, outer group of up to N_o / L slices), sums each slice's
+ *     dQ over the key range and the dbias of its (query, key) block over the whole outer
+ *     group inside the workgroup: J_K = ceil(N / 384) dQ partials and L <= 64 dbias
+ *     partials (L = 8 at N = 768), a small fraction of the single-pass kernel's partial
+ *     bytes.
  * Either way every sum has a fixed order, so results are bitwise reproducible.
  */
 tri_attn_status tri_attn_bwd(const tri_attn_dims* d,
@@ -222,10 +223,10 @@ int64_t tri_attn_noalloc_scratch_bytes(void);
 /*
  * Partial-buffer sizes of tri_attn_bwd for these dimensions (elements, FP32), the number
  * of dQ partials J_K and of dbias partials L, and the key-tile / outer-group sizes behind
- * them.  D = 16, 64 (single-pass kernel): key tile 128; group G = 6 for D = 16 with N
- * even, 4 with N odd, 2 for D = 64.  D = 32 (two kernels): the key range of the
- * query-tile kernel (128, 256 or 384 keys; J_K = ceil(N / 384) ranges) and its
- * outer group (L <= 64 groups).  Any output pointer may be NULL.  Host-only arithmetic;
+ * them.  Single-pass kernel (D = 64; D = 16 with N <= 640): key tile 128; group G = 6 for
+ * D = 16 with N even, 4 with N odd, 2 for D = 64.  Two kernels (D = 32; D = 16 with
+ * N > 640): the key range of the query-tile kernel (128, 256 or 384 keys;
+ * J_K = ceil(N / 384) ranges) and its outer group (L <= 64 groups).  Any output pointer may be NULL.  Host-only arithmetic;
  * no device access.
  */
 tri_attn_status tri_attn_workspace(const tri_attn_dims* d, int64_t* dq_partial_elems,

@@ -38,13 +38,13 @@ int64_t n_groups(const tri_attn_dims* d) { return (d->N_o + group_size(d) - 1) /
 int64_t x_elems(const tri_attn_dims* d) { return d->B * d->N_o * d->H * d->N * d->D; }
 int64_t y_elems(const tri_attn_dims* d) { return d->B * d->H * d->N * d->N; }
 
-// The default FP32 backward runs as two kernels for D = 32 (the key-tile kernel for dK, dV
-// and the query-tile kernel for dQ, dbias); D = 16 and 64, the bf16-partial variant and the
-// chunked backward use the single-pass key-tile kernel.  Partial counts of each design:
-// Two kernels (dK/dV key-tile, dQ/dbias query-tile) for D = 32, and for D = 16 past N = 640:
-// below that the single-pass kernel's partials are small enough that the second evaluation
-// of the scores does not pay (measured at N = 384 / 640 / 768: 0.291 / 1.171 / 1.913 ms per
-// step single-pass against 0.300 / 1.171 / 1.788 ms with two kernels).
+// The default FP32 backward runs as two kernels (the key-tile kernel for dK, dV and the
+// query-tile kernel for dQ, dbias) for D = 32, and for D = 16 past N = 640: below that the
+// single-pass kernel's partials are small enough that the second evaluation of the scores
+// does not pay (D = 16, measured at N = 384 / 640 / 768: 0.291 / 1.171 / 1.913 ms per step
+// single-pass against 0.300 / 1.171 / 1.788 ms with two kernels).  D = 64, the bf16-partial
+// variant and the chunked backward use the single-pass key-tile kernel.  Partial counts of
+// each design:
 bool two_kernel(const tri_attn_dims* d) { return d->D == 32 || (d->D == 16 && d->N > 640); }
 tri::BwdQPlan q_plan(const tri_attn_dims* d) { return tri::bwdq_plan(d->B, d->N_o, d->H, d->N); }
 int64_t dq_parts(const tri_attn_dims* d) { return two_kernel(d) ? q_plan(d).n_ranges : n_key_tiles(d); }
