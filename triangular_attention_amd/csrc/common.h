@@ -131,20 +131,25 @@ __device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds
 // waits vmcnt(0) just before the barrier that ends stage s - 1; the other set's
 // loads stay in flight across that barrier and are waited for a stage later.
 // rsrc: buffer descriptor words (wave-uniform); lds: wave-uniform LDS address (M0).
+// The compiler does not insert hazard wait states in front of inline assembly, so the
+// asm carries its own: on GFX9 a vector-memory instruction that reads an SGPR written
+// by a VALU instruction (v_readlane restoring a spilled SGPR, v_readfirstlane) needs 5
+// wait states after that write, which also covers the 1 a write of M0 needs before an
+// LDS-DMA load.  Without them the load can read a stale descriptor word.
 __device__ __forceinline__ u32x4 make_rsrc_words(const void* base, uint32_t bytes) {
   const uint64_t b = (uint64_t)base;
   return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 __device__ __forceinline__ void dma16(u32x4 rsrc, const void* lds, uint32_t off) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(lds);
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(m0), "v"(off), "s"(rsrc) : "memory");
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(m0), "v"(off), "s"(rsrc) : "memory");
 }
 
 // The 4-byte form (lane l's 4 bytes land at `lds + 4 * l`), for rows that are only
 // 4-byte aligned in memory.
 __device__ __forceinline__ void dma4(u32x4 rsrc, const void* lds, uint32_t off) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(lds);
-  asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"{m0}"(m0), "v"(off), "s"(rsrc) : "memory");
+  asm volatile("s_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"{m0}"(m0), "v"(off), "s"(rsrc) : "memory");
 }
 
 template <typename T> __device__ __forceinline__ T ld_shared(const uint16_t* p) {
