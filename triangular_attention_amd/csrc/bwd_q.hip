@@ -125,7 +125,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
   const float c1 = scale * kLog2e;
   const float kill = scale > 0.f ? -INFINITY : INFINITY;   // (bias + mask) / scale of absent keys
 
-  auto slice_row = [&](int o) { return (((int64_t)b * N_o + o) * H + h) * N; };
+  // Slice o's rows start at row ((b N_o + o) H + h) N of the [B, N_o, H, N] arrays; the
+  // per-slice offsets below advance by a stride instead of being formed again per slice.
+  const int64_t hn = (int64_t)H * N;
+  const int64_t sr0 = (((int64_t)b * N_o + o0) * H + h) * N;
   const uint32_t kv_bytes = (uint32_t)N * D * 2;
 
   // ---- bias / scale of the lane's (key, query) pairs, for the whole kernel
@@ -156,14 +159,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
       }
 
   // ---- staging of slice o into buffer buf (direct loads; rows past N read as zero)
-  auto stage = [&](int o, int buf) {
-    const int64_t sr = slice_row(o);
+  auto stage = [&](int64_t sr, const float* mrow, int buf) {
     const u32x4 rk = make_rsrc_words(a.k + sr * D, kv_bytes);
 #pragma unroll
     for (int i = 0; i < KDMA; ++i)
       dma16(rk, sK[buf][w] + 512 * i, (uint32_t)kw0 * D * 2 + k_src<D>(64 * i + lane));
     if constexpr (MASK) {
-      const u32x4 rm = make_rsrc_words(a.mask + ((int64_t)b * N_o + o) * N, (uint32_t)N * 4);
+      const u32x4 rm = make_rsrc_words(mrow, (uint32_t)N * 4);
 #pragma unroll
       for (int i = 0; i < MW / 64; ++i) dma4(rm, sM[buf][w] + 64 * i, (uint32_t)(kw0 + 64 * i + lane) * 4);
     }
@@ -183,8 +185,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
     }
   };
   // V rows of pair p (blocks e = 0, 1) of slice o: the A operands of dP^T = V dO^T
-  auto load_v = [&](int o, int p, QT (&vb)[2]) {
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + slice_row(o) * D, kv_bytes);
+  auto load_v = [&](int64_t sr, int p, QT (&vb)[2]) {
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + sr * D, kv_bytes);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int key = kw0 + 32 * p + 8 * (c >> 2) + 4 * e + (c & 3);
@@ -196,11 +198,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
   // the workgroup's dQ rows of slice o: item tid of the summed tile, stored in the key
   // range's FP32 partial; rows past N fall outside the descriptor's extent
   const int64_t part_rows = (int64_t)a.B * N_o * H * N;
-  auto store_dq = [&](int o, f32x4 v) {
+  auto store_dq = [&](int64_t sr, f32x4 v) {
     if (tid < RED) {
       const int row = tid / (D / 4), c4 = tid % (D / 4);
       const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(a.dq_partial + (r * part_rows + slice_row(o) + q0) * D, (uint32_t)(N - q0) * D * 4);
+          make_rsrc(a.dq_partial + (r * part_rows + sr + q0) * D, (uint32_t)(N - q0) * D * 4);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (uint32_t)(row * D + 4 * c4) * 4,
                                              0, 0);
     }
@@ -208,23 +210,25 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
 
   // ---- prologue: slice o0 staged, V of its first pair in registers
   QT vcur[2], vnxt[2];
-  stage(o0, 0);
-  load_v(o0, 0, vcur);
+  const float* mrow = MASK ? a.mask + ((int64_t)b * N_o + o0) * N : nullptr;   // slice o0's mask row
+  stage(sr0, mrow, 0);
+  load_v(sr0, 0, vcur);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   lds_barrier();
 
   f32x4 red = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ns; ++s) {
+  int64_t sr = sr0;                              // slice o0 + s's row offset
+  for (int s = 0; s < ns; ++s, sr += hn) {
     const int buf = s & 1;
-    const int o = o0 + s;
     if (s > 0) {
-      // slice o's tiles landed (each wave's own loads) and visible to all; every wave has
-      // read the previous dQ^T tiles
+      // slice o0 + s's tiles landed (each wave's own loads) and visible to all; every wave
+      // has read the previous dQ^T tiles
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
       lds_barrier();
-      store_dq(o - 1, red);
+      store_dq(sr - hn, red);
     }
-    if (s + 1 < ns) stage(o + 1, buf ^ 1);
+    if (MASK) mrow += N;
+    if (s + 1 < ns) stage(sr + hn, mrow, buf ^ 1);
 
     // the slice's -lse log2(e) and -delta of the lane's queries
     float nl[NQB];
@@ -250,8 +254,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
       // slice; the compiler barrier keeps them from being merged with the previous pair's)
       asm volatile("" ::: "memory");
       // V of the next pair, or of the next slice's first pair
-      if (p + 1 < NP) load_v(o, p + 1, vnxt);
-      else if (s + 1 < ns) load_v(o + 1, 0, vnxt);
+      if (p + 1 < NP) load_v(sr, p + 1, vnxt);
+      else if (s + 1 < ns) load_v(sr + hn, 0, vnxt);
       if (kw0 + 32 * p < N) {      // wave-uniform: the pair holds keys
         QT ka[2];
         f32x4 mk[2];
@@ -315,7 +319,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
       red = acc * scale;
     }
   }
-  store_dq(o0 + ns - 1, red);
+  store_dq(sr0 + (ns - 1) * hn, red);
 
   // ---- this group's dbias partial of the (query, key) block: keys 32p + 8g + 4e + 0..3 of
   // the wave at query 16qb + c; entries past N fall outside the plane's extent
