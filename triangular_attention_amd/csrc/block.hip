@@ -69,10 +69,11 @@ __global__ __launch_bounds__(NT) void ln_proj_kernel(BlkLnProjArgs a) {
 
   u32x4 zv[4];
   auto load_z = [&](int tile) {
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int r = tile * TP + 16 * w + 4 * s + g;
-      const uint32_t off = r < total ? (uint32_t)zrow(pair_ix(r, N), N, ending) * 2 + 16 * c : zbytes;
+      const int l = 16 * w + 4 * s + g;
+      const uint32_t off = tile_ok(tr, l, total) ? (uint32_t)zrow_t(tr, l, N, ending) * 2 + 16 * c : zbytes;
       zv[s] = buf_ld16(zr, off);
     }
   };
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(NT) void ln_proj_kernel(BlkLnProjArgs a) {
   int it = 0;
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x, ++it) {
     uint16_t* buf = sZ[it & 1];
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       float x[8];
@@ -116,15 +118,13 @@ __global__ __launch_bounds__(NT) void ln_proj_kernel(BlkLnProjArgs a) {
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int fb = 0; fb < 4; ++fb) acc[fb] = mfma_k32(wf[fb][s], bf[s], acc[fb]);
-      const int r = tile * TP + rl;
-      const bool ok = r < total;
-      const PairIx p = pair_ix(ok ? r : 0, N);
+      const bool ok = tile_ok(tr, rl, total);
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb) {
         const int hd0 = 64 * (w & 1) + 16 * fb;
         const int h = hd0 / D, d0 = hd0 % D + 4 * g;
         if (ok)
-          *reinterpret_cast<u32x2*>(outp + hm_off<H, D>(p, N, h, d0)) =
+          *reinterpret_cast<u32x2*>(outp + hm_off_t<H, D>(tr, rl, N, h, d0)) =
               u32x2{pack_bf16(acc[fb][0], acc[fb][1]), pack_bf16(acc[fb][2], acc[fb][3])};
       }
     }
@@ -135,13 +135,11 @@ __global__ __launch_bounds__(NT) void ln_proj_kernel(BlkLnProjArgs a) {
       f32x4 ab = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) ab = mfma_k32(wb[s], ld_lds16(buf, toff(rl, 4 * s + g)), ab);
-      const int r = tile * TP + rl;
-      if (r < total) {
-        const PairIx p = pair_ix(r, N);
+      if (tile_ok(tr, rl, total)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int h = 4 * g + i;
-          if (h < H) a.bias[((p.b * H + h) * N + p.x) * N + p.y] = f_to_bf(ab[i]);
+          if (h < H) a.bias[bias_off_t<H>(tr, rl, N, h)] = f_to_bf(ab[i]);
         }
       }
     }
@@ -191,12 +189,12 @@ __global__ __launch_bounds__(NT) void gate_out_kernel(BlkGateOutArgs a) {
 
   u32x4 ov[4], gv[4];
   auto load = [&](int tile) {
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int p, h, dc;
       hm_chunk<H, D>(t, i, TP, p, h, dc);
-      const int r = tile * TP + p;
-      const uint32_t off = r < total ? (uint32_t)hm_off<H, D>(pair_ix(r, N), N, h, 8 * dc) * 2 : hbytes;
+      const uint32_t off = tile_ok(tr, p, total) ? (uint32_t)hm_off_t<H, D>(tr, p, N, h, 8 * dc) * 2 : hbytes;
       ov[i] = buf_ld16(orr, off);
       gv[i] = buf_ld16(grr, off);
     }
@@ -205,6 +203,7 @@ __global__ __launch_bounds__(NT) void gate_out_kernel(BlkGateOutArgs a) {
   int it = 0;
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x, ++it) {
     uint16_t* buf = sGO[it & 1];
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int p, h, dc;
@@ -220,9 +219,8 @@ __global__ __launch_bounds__(NT) void gate_out_kernel(BlkGateOutArgs a) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc = mfma_k32(wo[s], ld_lds16(buf, toff(rl, 4 * s + g)), acc);
-      const int r = tile * TP + rl;
-      if (r < total)
-        *reinterpret_cast<u32x2*>(a.y + zrow(pair_ix(r, N), N, ending) + 16 * w + 4 * g) =
+      if (tile_ok(tr, rl, total))
+        *reinterpret_cast<u32x2*>(a.y + zrow_t(tr, rl, N, ending) + 16 * w + 4 * g) =
             u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
     }
   }
@@ -263,15 +261,14 @@ __global__ __launch_bounds__(NT) void gate_out_bwd_kernel(BlkGateOutArgs a) {
 
   u32x4 yv[4], ov[4], gv[4];
   auto load = [&](int tile) {
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = t + NT * i, p = q >> 4, j = q & 15;
-      const int r = tile * TP + p;
-      yv[i] = buf_ld16(yr, r < total ? (uint32_t)zrow(pair_ix(r, N), N, ending) * 2 + 16 * j : ybytes);
+      yv[i] = buf_ld16(yr, tile_ok(tr, p, total) ? (uint32_t)zrow_t(tr, p, N, ending) * 2 + 16 * j : ybytes);
       int ph, h, dc;
       hm_chunk<H, D>(t, i, TP, ph, h, dc);
-      const int r2 = tile * TP + ph;
-      const uint32_t off = r2 < total ? (uint32_t)hm_off<H, D>(pair_ix(r2, N), N, h, 8 * dc) * 2 : hbytes;
+      const uint32_t off = tile_ok(tr, ph, total) ? (uint32_t)hm_off_t<H, D>(tr, ph, N, h, 8 * dc) * 2 : hbytes;
       ov[i] = buf_ld16(orr, off);
       gv[i] = buf_ld16(grr, off);
     }
@@ -291,6 +288,7 @@ __global__ __launch_bounds__(NT) void gate_out_bwd_kernel(BlkGateOutArgs a) {
   };
   if ((int)blockIdx.x < ntiles) load(blockIdx.x);
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const TileRows tr = tile_rows(tile, TP, N, total);
     lds_barrier();            // the previous tile's reads are done
     stash();
     const int nt = tile + gridDim.x;
@@ -317,9 +315,8 @@ __global__ __launch_bounds__(NT) void gate_out_bwd_kernel(BlkGateOutArgs a) {
         dov[i] = acc[i] * sg;
         dgv[i] = acc[i] * of[i] * (sg * (1.f - sg));
       }
-      const int r = tile * TP + rl;
-      if (r < total) {
-        const int off = hm_off<H, D>(pair_ix(r, N), N, h, d0);
+      if (tile_ok(tr, rl, total)) {
+        const int off = hm_off_t<H, D>(tr, rl, N, h, d0);
         *reinterpret_cast<u32x2*>(a.d_o + off) = u32x2{pack_bf16(dov[0], dov[1]), pack_bf16(dov[2], dov[3])};
         *reinterpret_cast<u32x2*>(a.d_g + off) = u32x2{pack_bf16(dgv[0], dgv[1]), pack_bf16(dgv[2], dgv[3])};
       }
@@ -355,22 +352,19 @@ struct ProjTileLoader {
   __device__ __forceinline__ void load(const BlkProjBwdArgs& a, int tile, int t, int total,
                                        const __amdgpu_buffer_rsrc_t* rs, uint32_t hbytes) {
     const int N = a.s.N;
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int i = 0; i < 2 * NSEG; ++i) {
       const int seg = i >> 1;                       // 1024 chunks per segment = 2 per thread
       int p, h, dc;
       hm_chunk<H, D>(t, i & 1, TP, p, h, dc);
-      const int r = tile * TP + p;
-      const uint32_t off = r < total ? (uint32_t)hm_off<H, D>(pair_ix(r, N), N, h, 8 * dc) * 2 : hbytes;
+      const uint32_t off = tile_ok(tr, p, total) ? (uint32_t)hm_off_t<H, D>(tr, p, N, h, 8 * dc) * 2 : hbytes;
       v[i] = buf_ld16(rs[seg], off);
     }
     bv = 0;
     if (t < TP * H) {
-      const int p = t % TP, h = t / TP, r = tile * TP + p;
-      if (r < total) {
-        const PairIx q = pair_ix(r, N);
-        bv = a.dbias[((q.b * H + h) * N + q.x) * N + q.y];
-      }
+      const int p = t % TP, h = t / TP;
+      if (tile_ok(tr, p, total)) bv = a.dbias[bias_off_t<H>(tr, p, N, h)];
     }
   }
   __device__ __forceinline__ void stash(uint16_t* sP, uint16_t* sB, int t) const {
@@ -436,17 +430,18 @@ __global__ __launch_bounds__(NT) void proj_dz_kernel(BlkProjBwdArgs a) {
   u32x2 zq[TP / 16];
   f32x2 st[TP / 16];
   auto load_own = [&](int tile) {      // this lane's Z features and statistics of its 4 pairs
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int pb = 0; pb < TP / 16; ++pb) {
-      const int r = tile * TP + 16 * pb + c;
-      const bool ok = r < total;
-      const PairIx p = pair_ix(ok ? r : 0, N);
-      zq[pb] = buf_ld8(zr, ok ? (uint32_t)(zrow(p, N, ending) + c0) * 2 : zbytes);
+      const int l = 16 * pb + c, r = tr.r0 + l;
+      const bool ok = tile_ok(tr, l, total);
+      zq[pb] = buf_ld8(zr, ok ? (uint32_t)(zrow_t(tr, l, N, ending) + c0) * 2 : zbytes);
       st[pb] = __builtin_bit_cast(f32x2, buf_ld8(sr, ok ? (uint32_t)r * 8 : (uint32_t)total * 8));
     }
   };
   if ((int)blockIdx.x < ntiles) { ld.load(a, blockIdx.x, t, total, rs, hbytes); load_own(blockIdx.x); }
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const TileRows tr = tile_rows(tile, TP, N, total);
     lds_barrier();
     ld.stash(sP, sB, t);
     u32x2 zc[TP / 16];
@@ -495,9 +490,8 @@ __global__ __launch_bounds__(NT) void proj_dz_kernel(BlkProjBwdArgs a) {
       float dz[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) dz[i] = sc[pb][1] * (gm[i] * acc[pb][i] - m1 - xh[pb][i] * m2);
-      const int r = tile * TP + rl;
-      if (r < total)
-        *reinterpret_cast<u32x2*>(a.dz + zrow(pair_ix(r, N), N, ending) + c0) =
+      if (tile_ok(tr, rl, total))
+        *reinterpret_cast<u32x2*>(a.dz + zrow_t(tr, rl, N, ending) + c0) =
             u32x2{pack_bf16(dz[0], dz[1]), pack_bf16(dz[2], dz[3])};
     }
   }
@@ -552,11 +546,12 @@ __global__ __launch_bounds__(NT) void proj_dw_kernel(BlkProjBwdArgs a) {
   u32x4 zv[2];
   f32x2 st[2];
   auto load_z = [&](int tile) {
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int r = tile * TP + (t >> 4) + 32 * i;
-      const bool ok = r < total;
-      zv[i] = buf_ld16(zr, ok ? (uint32_t)zrow(pair_ix(ok ? r : 0, N), N, ending) * 2 + 16 * zj : zbytes);
+      const int l = (t >> 4) + 32 * i, r = tr.r0 + l;
+      const bool ok = tile_ok(tr, l, total);
+      zv[i] = buf_ld16(zr, ok ? (uint32_t)zrow_t(tr, l, N, ending) * 2 + 16 * zj : zbytes);
       st[i] = __builtin_bit_cast(f32x2, buf_ld8(sr, ok ? (uint32_t)r * 8 : (uint32_t)total * 8));
     }
   };

@@ -60,6 +60,48 @@ __device__ __forceinline__ int hm_off(const PairIx& p, int N, int h, int d) {
   return ((p.b * N + p.x) * H + h) * N * D + p.y * D + d;
 }
 
+// The pairs of one tile, r0 = tile * TP .. r0 + TP - 1, where pair r = (b N + x) N + y.  When they
+// all lie in one row (b, x) of the pair grid and inside the problem (always so when TP divides N),
+// pair l of the tile is (b, x, y0 + l) and its offsets need no division: one division pair per
+// tile replaces one per pair and load (each an integer-division sequence of some twenty vector
+// instructions).  Otherwise (rows shorter than a tile, the last tile) every pair is divided out.
+// The struct depends only on the tile, so `one` is the same for the whole workgroup.  The fast
+// forms use 24-bit products, so they are also limited to B N < 2^23 rows.
+struct TileRows {
+  int r0, b, x, y0;
+  bool one;
+};
+__device__ __forceinline__ TileRows tile_rows(int tile, int TP, int N, int total) {
+  TileRows t;
+  t.r0 = tile * TP;
+  const PairIx p = pair_ix(t.r0 < total ? t.r0 : 0, N);
+  t.b = p.b;
+  t.x = p.x;
+  t.y0 = p.y;
+  t.one = t.r0 + TP <= total && p.y + TP <= N && (total >> 23) < N;
+  return t;
+}
+// Pair l (< TP) of the tile is inside the problem.
+__device__ __forceinline__ bool tile_ok(const TileRows& t, int l, int total) { return t.one || t.r0 + l < total; }
+// zrow of pair l of the tile (the pair must be inside the problem)
+__device__ __forceinline__ int zrow_t(const TileRows& t, int l, int N, int ending) {
+  if (t.one) return ending ? (__mul24(t.b * N + t.y0 + l, N) + t.x) * 128 : (t.r0 + l) * 128;
+  return zrow(pair_ix(t.r0 + l, N), N, ending);
+}
+// hm_off of pair l of the tile (the pair must be inside the problem)
+template <int H, int D>
+__device__ __forceinline__ int hm_off_t(const TileRows& t, int l, int N, int h, int d) {
+  if (t.one) return (t.b * N + t.x) * (H * N * D) + __mul24(h, N * D) + (t.y0 + l) * D + d;
+  return hm_off<H, D>(pair_ix(t.r0 + l, N), N, h, d);
+}
+// Element offset of pair l's entry of head h in a [B, H, N, N] tensor (the pair bias)
+template <int H>
+__device__ __forceinline__ int bias_off_t(const TileRows& t, int l, int N, int h) {
+  if (t.one) return (t.b * H * N + t.x) * N + t.y0 + l + h * (N * N);
+  const PairIx p = pair_ix(t.r0 + l, N);
+  return ((p.b * H + h) * N + p.x) * N + p.y;
+}
+
 __device__ __forceinline__ void unpack8(u32x4 v, float* f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { f[2 * i] = bf_lo(v[i]); f[2 * i + 1] = bf_hi(v[i]); }

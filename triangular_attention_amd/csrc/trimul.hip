@@ -43,6 +43,11 @@ __device__ __forceinline__ int cm_off(int r, int ch, int nn, int c) {
   const int b = r / nn;
   return (b * c + ch) * nn + (r - b * nn);
 }
+// the same for pair l of a tile (TileRows: no division when the tile lies in one row)
+__device__ __forceinline__ int cm_off_t(const TileRows& t, int l, int ch, int nn, int c) {
+  if (t.one) return t.b * (c - 1) * nn + t.r0 + l + ch * nn;
+  return cm_off(t.r0 + l, ch, nn, c);
+}
 
 // [channel][pair] LDS tiles: rows of 128 pairs padded to 144 elements (row stride 8 banks), so
 // the transposing reads of 4 rows are conflict-free and a pair-block offset is a constant
@@ -103,16 +108,18 @@ __global__ __launch_bounds__(NT) void tm_in_fwd_kernel(TmInArgs a) {
 
   u32x4 zv[4];
   auto load_z = [&](int tile) {
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int r = tile * TP + 16 * w + 4 * s + g;
-      zv[s] = buf_ld16(zr, r < total ? (uint32_t)zrow(pair_ix(r, N), N, inc) * 2 + 16 * c : zbytes);
+      const int l = 16 * w + 4 * s + g;
+      zv[s] = buf_ld16(zr, tile_ok(tr, l, total) ? (uint32_t)zrow_t(tr, l, N, inc) * 2 + 16 * c : zbytes);
     }
   };
   if ((int)blockIdx.x < ntiles) load_z(blockIdx.x);
   int iter = 0;
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x, ++iter) {
     uint16_t* buf = sZ[iter & 1];
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       float x[8];
@@ -162,9 +169,8 @@ __global__ __launch_bounds__(NT) void tm_in_fwd_kernel(TmInArgs a) {
       f32x4 go = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) go = mfma_k32(wo[s], bf[s], go);
-      const int r = tile * TP + rl;
-      if (r < total)
-        *reinterpret_cast<u32x2*>(a.g + zrow(pair_ix(r, N), N, inc) + 16 * w + 4 * g) =
+      if (tile_ok(tr, rl, total))
+        *reinterpret_cast<u32x2*>(a.g + zrow_t(tr, rl, N, inc) + 16 * w + 4 * g) =
             u32x2{pack_bf16(go[0], go[1]), pack_bf16(go[2], go[3])};
     }
     lds_barrier();
@@ -175,8 +181,8 @@ __global__ __launch_bounds__(NT) void tm_in_fwd_kernel(TmInArgs a) {
 #pragma unroll
       for (int k = 0; k < NSTORE; ++k) {
         const int q = t + NT * k, ch = q >> 4, seg = q & 15;
-        const int r0 = tile * TP + 8 * seg;
-        if (r0 < total) *reinterpret_cast<u32x4*>(dst + cm_off(r0, ch, nn, CH)) = ld_lds16(sAB[kd], coff(ch, 8 * seg));
+        if (tr.r0 + 8 * seg < total)
+          *reinterpret_cast<u32x4*>(dst + cm_off_t(tr, 8 * seg, ch, nn, CH)) = ld_lds16(sAB[kd], coff(ch, 8 * seg));
       }
     }
   }
@@ -217,18 +223,18 @@ __global__ __launch_bounds__(NT) void tm_in_bwd_kernel(TmInArgs a) {
   u32x4 zv[4], dv[2][NLD];
   f32x2 st[4];
   auto load = [&](int tile) {
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int r = tile * TP + 16 * w + 4 * s + g;
-      const bool ok = r < total;
-      zv[s] = buf_ld16(zr, ok ? (uint32_t)zrow(pair_ix(r, N), N, inc) * 2 + 16 * c : zbytes);
+      const int l = 16 * w + 4 * s + g, r = tr.r0 + l;
+      const bool ok = tile_ok(tr, l, total);
+      zv[s] = buf_ld16(zr, ok ? (uint32_t)zrow_t(tr, l, N, inc) * 2 + 16 * c : zbytes);
       st[s] = __builtin_bit_cast(f32x2, buf_ld8(sr, ok ? (uint32_t)r * 8 : (uint32_t)total * 8));
     }
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
       const int q = t + NT * k, ch = q >> 4, seg = q & 15;
-      const int r0 = tile * TP + 8 * seg;
-      const uint32_t off = r0 < total ? (uint32_t)cm_off(r0, ch, nn, CH) * 2 : cbytes;
+      const uint32_t off = tr.r0 + 8 * seg < total ? (uint32_t)cm_off_t(tr, 8 * seg, ch, nn, CH) * 2 : cbytes;
       dv[0][k] = buf_ld16(dar, off);
       dv[1][k] = buf_ld16(dbr, off);
     }
@@ -414,11 +420,11 @@ __global__ __launch_bounds__(NT, CH == 64 ? 4 : 2) void tm_out_fwd_kernel(TmOutA
   u32x4 xv[NLD];
   u32x2 gv[TP / 16];        // this lane's gate logits of the tile (4 features of one pair per block)
   auto load = [&](int tile) {
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
       const int q = t + NT * k, ch = q >> 4, seg = q & 15;
-      const int r0 = tile * TP + 8 * seg;
-      xv[k] = buf_ld16(xr, r0 < total ? (uint32_t)cm_off(r0, ch, nn, CH) * 2 : xbytes);
+      xv[k] = buf_ld16(xr, tr.r0 + 8 * seg < total ? (uint32_t)cm_off_t(tr, 8 * seg, ch, nn, CH) * 2 : xbytes);
     }
 #pragma unroll
     for (int pb = 0; pb < TP / 16; ++pb) {
@@ -543,11 +549,11 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
   // this lane's incoming gradient and gate logits (4 features of one pair per block)
   u32x2 dln[TP / 16], gln[TP / 16];
   auto load = [&](int tile) {
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
       const int q = t + NT * k, ch = q / SEGS, seg = q % SEGS;
-      const int r0 = tile * TP + 8 * seg;
-      xv[k] = buf_ld16(xr, r0 < total ? (uint32_t)cm_off(r0, ch, nn, CH) * 2 : xbytes);
+      xv[k] = buf_ld16(xr, tr.r0 + 8 * seg < total ? (uint32_t)cm_off_t(tr, 8 * seg, ch, nn, CH) * 2 : xbytes);
     }
     const int rp = tile * TP + pp;
     stv = __builtin_bit_cast(f32x2, buf_ld8(sr, rp < total ? (uint32_t)rp * 8 : (uint32_t)total * 8));
@@ -683,8 +689,9 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
       const int q = t + NT * k, ch = q / SEGS, seg = q % SEGS;
-      const int r0 = tile * TP + 8 * seg;
-      if (r0 < total) *reinterpret_cast<u32x4*>(a.dx + cm_off(r0, ch, nn, CH)) = ld_lds16(sXL, coff(ch, 8 * seg));
+      const TileRows tr = tile_rows(tile, TP, N, total);
+      if (tr.r0 + 8 * seg < total)
+        *reinterpret_cast<u32x4*>(a.dx + cm_off_t(tr, 8 * seg, ch, nn, CH)) = ld_lds16(sXL, coff(ch, 8 * seg));
     }
   }
   // partials: d w_o [C][CH]; d gamma_o / d beta_o per (workgroup, wave half)
@@ -742,17 +749,18 @@ __global__ __launch_bounds__(NT) void tm_in_dz_kernel(TmInGradArgs a) {
   f32x2 st[2][TP / 16];
   auto load = [&](int tile, auto k_c) {
     constexpr int K = decltype(k_c)::value;
-    const int r = tile * TP + lp;
-    const bool ok = r < total;
+    const TileRows tr = tile_rows(tile, TP, N, total);
+    const int r = tr.r0 + lp;
+    const bool ok = tile_ok(tr, lp, total);
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
       pv[K][s] = buf_ld16(pr, ok ? (uint32_t)((size_t)r * 4 * CH + 128 * s + 8 * lj) * 2 : pbytes);
-    pv[K][NS - 1] = buf_ld16(gr, ok ? (uint32_t)(zrow(pair_ix(r, N), N, inc) + 8 * lj) * 2 : zbytes);
+    pv[K][NS - 1] = buf_ld16(gr, ok ? (uint32_t)(zrow_t(tr, lp, N, inc) + 8 * lj) * 2 : zbytes);
 #pragma unroll
     for (int pb = 0; pb < TP / 16; ++pb) {
-      const int rr = tile * TP + 16 * pb + c;
-      const bool ok2 = rr < total;
-      zq[K][pb] = buf_ld8(zr, ok2 ? (uint32_t)(zrow(pair_ix(rr, N), N, inc) + c0) * 2 : zbytes);
+      const int l = 16 * pb + c, rr = tr.r0 + l;
+      const bool ok2 = tile_ok(tr, l, total);
+      zq[K][pb] = buf_ld8(zr, ok2 ? (uint32_t)(zrow_t(tr, l, N, inc) + c0) * 2 : zbytes);
       st[K][pb] = __builtin_bit_cast(f32x2, buf_ld8(sr, ok2 ? (uint32_t)rr * 8 : (uint32_t)total * 8));
     }
   };
@@ -763,6 +771,7 @@ __global__ __launch_bounds__(NT) void tm_in_dz_kernel(TmInGradArgs a) {
   if ((int)blockIdx.x + gs < ntiles) load(blockIdx.x + gs, S1{});
   auto body = [&](int tile, auto k_c) {
     constexpr int K = decltype(k_c)::value;
+    const TileRows trs = tile_rows(tile, TP, N, total);
     lds_barrier();
 #pragma unroll
     for (int s = 0; s < NS; ++s) st_lds16(sP[s], toff(lp, lj), pv[K][s]);
@@ -809,9 +818,8 @@ __global__ __launch_bounds__(NT) void tm_in_dz_kernel(TmInGradArgs a) {
       float dz[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) dz[i] = sc[pb][1] * (gm[i] * acc[pb][i] - m1 - xh[pb][i] * m2);
-      const int r = tile * TP + rl;
-      if (r < total)
-        *reinterpret_cast<u32x2*>(a.dz + zrow(pair_ix(r, N), N, inc) + c0) =
+      if (tile_ok(trs, rl, total))
+        *reinterpret_cast<u32x2*>(a.dz + zrow_t(trs, rl, N, inc) + c0) =
             u32x2{pack_bf16(dz[0], dz[1]), pack_bf16(dz[2], dz[3])};
     }
   };
@@ -860,15 +868,16 @@ __global__ __launch_bounds__(NT) void tm_in_dw_kernel(TmInGradArgs a) {
   u32x4 pv[2], zv[2];
   f32x2 st[2];
   auto load = [&](int tile) {
+    const TileRows tr = tile_rows(tile, TP, N, total);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int pl = (t >> 4) + 32 * i, r = tile * TP + pl;
-      const bool ok = r < total;
-      const PairIx pi = pair_ix(ok ? r : 0, N);
-      const uint32_t poff = from_gate ? (uint32_t)(zrow(pi, N, inc) + 8 * zj) * 2
+      const int pl = (t >> 4) + 32 * i, r = tr.r0 + pl;
+      const bool ok = tile_ok(tr, pl, total);
+      const int zo = ok ? zrow_t(tr, pl, N, inc) : 0;
+      const uint32_t poff = from_gate ? (uint32_t)(zo + 8 * zj) * 2
                                       : (uint32_t)((size_t)r * 4 * CH + 128 * split + 8 * zj) * 2;
       pv[i] = buf_ld16(pr, ok ? poff : (from_gate ? zbytes : pbytes));
-      zv[i] = buf_ld16(zr, ok ? (uint32_t)zrow(pi, N, inc) * 2 + 16 * zj : zbytes);
+      zv[i] = buf_ld16(zr, ok ? (uint32_t)zo * 2 + 16 * zj : zbytes);
       st[i] = __builtin_bit_cast(f32x2, buf_ld8(sr, ok ? (uint32_t)r * 8 : (uint32_t)total * 8));
     }
   };
