@@ -7,9 +7,15 @@
 namespace tri {
 namespace pair {
 
-// Chunk swizzle of a 256-byte row: rows r and r' of any aligned group of 16 get
-// different XOR masks; within an aligned group of 4 rows the masks differ in bits 1-2 only.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1); }
+// Chunk swizzle of a 256-byte row (16 chunks of 16 bytes).  gfx950 serves an LDS access as two
+// 32-lane halves; a half is conflict-free when its 16-byte slots are distinct modulo 512 bytes
+// (16-byte accesses) or its 8-byte units distinct modulo 256 bytes (8-byte accesses).  The XOR
+// mask below, a linear map of the row's low four bits, makes every access shape of the pair
+// kernels conflict-free under that rule (checked exhaustively on the host): MFMA operand reads
+// (16 consecutive rows, chunks 2k and 2k + 1 in a half), transposing reads (rows 8g + 0..3 and
+// + 4, two adjacent chunks, both 8-byte halves), 8-byte reads of one chunk of 16 rows, and
+// stores of 8 rows x 4 chunks, 16 rows x 2 chunks or 2 rows x 16 chunks.
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) ^ (-((r >> 3) & 1) & 11); }
 // element offset of logical 16-byte chunk j (0..15) of row r in a [rows][128] bf16 tile
 __device__ __forceinline__ int toff(int r, int j) { return r * 128 + ((j ^ swz(r)) << 3); }
 
