@@ -30,6 +30,7 @@ CASES = [
     (1, 40, 4, True, 0.1),
     (1, 182, 4, False, 0.08),
     (1, 182, 8, True, 0.08),
+    (2, 128, 4, True, 0.08),     # B = 2 with whole-row tiles: the division-free index path at b = 1
 ]
 
 

@@ -30,6 +30,7 @@ CASES = [
     (1, 40, 128, False, 0.1),
     (1, 136, 128, False, 0.08),
     (1, 136, 64, True, 0.08),
+    (2, 128, 64, False, 0.08),   # B = 2 with whole-row tiles: the division-free index path at b = 1
 ]
 
 
