@@ -643,6 +643,7 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
 #pragma unroll
     for (int h = 0; h < NPB / KC; ++h) {
       f32x4 acc2[KC];
+      float xhk[KC][4];
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
         const int rl = 16 * (pb0 + KC * h + k) + c;
@@ -651,7 +652,7 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
         for (int s = 0; s < 4; ++s)
           s4 = mfma_k32(ld_lds16(sWT, toff(chb * 16 + c, 4 * s + g)), ld_lds16(sDP, toff(rl, 4 * s + g)), s4);
         acc2[k] = s4;
-        float xh[4];
+        float* xh = xhk[k];
         xhat4(rl, xh);
         float p1 = 0.f, p2 = 0.f;
 #pragma unroll
@@ -676,8 +677,7 @@ __global__ __launch_bounds__(NT) void tm_out_bwd_kernel(TmOutArgs a) {
         for (int v = 0; v < CH / 16; ++v) { m1 += sRed[w0 + v][rl][0]; m2 += sRed[w0 + v][rl][1]; }
         m1 *= 1.f / CH;
         m2 *= 1.f / CH;
-        float xh[4];
-        xhat4(rl, xh);
+        const float* xh = xhk[k];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ch = chb * 16 + 4 * g + i;
