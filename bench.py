@@ -566,7 +566,7 @@ def _traffic_lookup(path, workload, dom, prefix):
         return None, None
     try:
         tr = json.load(open(path)).get(workload, {})
-        if tr.get("kernel_hash") != kernel_hash(None):
+        if tr.get("kernel_hash") != kernel_hash(_hash_files(workload)):
             return None, None
         allk = tr["kernels"]
         for kname, val in allk.items():
@@ -729,7 +729,7 @@ def bench_block(args, bw, dev):
     if os.path.exists(args.traffic):
         try:
             tr = json.load(open(args.traffic)).get(bw.name, {})
-            if tr.get("kernel_hash") == kernel_hash(None):
+            if tr.get("kernel_hash") == kernel_hash(_hash_files(bw.name)):
                 traffic_all = tr["kernels"]
                 for kname, val in traffic_all.items():
                     if kname.startswith(dom + "_kernel"):
@@ -889,12 +889,20 @@ def bench_trimul(args, tw, dev):
 
 
 def _hash_files(workload):
-    return None if workload.startswith(("block", "trimul")) else ATTN_SOURCES
+    """The sources of the kernels a workload runs: the block runs the attention kernels too;
+    the triangle update's weight-gradient reductions are the block's reduce kernel."""
+    if workload.startswith("block"):
+        return ATTN_SOURCES + BLOCK_SOURCES
+    if workload.startswith("trimul"):
+        return TRIMUL_SOURCES
+    return ATTN_SOURCES
 
 
 ATTN_SOURCES = ("common.h", "kernels.h", "bwd_layout.h", "api.hip", "fwd.hip", "bwd.hip", "bwd_q.hip",
                 "delta_reduce.hip")
-BLOCK_SOURCES = ("common.h", "block_kernels.h", "block_api.hip", "block.hip")
+BLOCK_SOURCES = ("block_kernels.h", "block_api.hip", "block.hip", "pair_common.h")
+TRIMUL_SOURCES = ("common.h", "pair_common.h", "trimul_kernels.h", "trimul_api.hip", "trimul.hip",
+                  "block_kernels.h", "block.hip")
 
 
 def kernel_hash(files=ATTN_SOURCES):
