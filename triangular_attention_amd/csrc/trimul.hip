@@ -298,20 +298,29 @@ __global__ __launch_bounds__(NT) void tm_in_bwd_kernel(TmInArgs a) {
 // The per-channel products.  C[b] = opA(b) opB(b) with M = N = K = n for every b (an example
 // and channel).  TA: A stored [k][m] (else [m][k]); TB: B stored [k][n] (else [n][k]).  The MFMA
 // forms C^T = opB^T opA^T so that a lane's four results are four consecutive n of one m.
-// 256 threads, 128 x 128 tile, waves 2 x 2 of 64 x 64, k step 32, operand tiles double-buffered.
-template <bool TA, bool TB>
+// 256 threads, MT x MT tile, waves 2 x 2 of MT/2 x MT/2, k step 32, operand tiles double-buffered.
+// MT = 192 when both operands are row-major and 192 divides n (4 x 4 tiles per matrix at n = 768:
+// with two workgroups per CU the 2048 tiles of 128 channels are exactly 4 rounds of the 256 CUs,
+// where 128 x 128 tiles left the last of 4.5 rounds half empty); 128 otherwise.
+template <bool TA, bool TB, int MT>
 __global__ __launch_bounds__(256) void tm_gemm_kernel(TmGemmArgs p) {
   constexpr int TK = 32;
-  __shared__ __align__(16) uint16_t sA[2][128 * TK];
-  __shared__ __align__(16) uint16_t sB[2][128 * TK];
+  constexpr int MB = MT / 32;          // 16-row blocks of a wave in m (a wave holds MT / 2 rows)
+  constexpr int LA = MT / 64;          // A-tile loads per thread
+  constexpr int NTT = MT;              // n rows of the tile (the B tile)
+  constexpr int NBB = NTT / 32;        // 16-column blocks of a wave in n
+  constexpr int LB = NTT / 64;
+  static_assert(MT == 128 || (MT == 192 && !TA && !TB), "192-row tiles only for row-major A and B");
+  __shared__ __align__(16) uint16_t sA[2][MT * TK];
+  __shared__ __align__(16) uint16_t sB[2][NTT * TK];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
   const int t = threadIdx.x;
-  const int N = p.N, nt = (N + 127) / 128, ntile = nt * nt;
+  const int N = p.N, ntm = (N + MT - 1) / MT, nt = (N + NTT - 1) / NTT, ntile = ntm * nt;
   // all tiles of one matrix on one XCD (blocks are dealt round-robin over 8 XCDs)
   const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
   const int bt = (kx / ntile) * 8 + xcd;
   if (bt >= p.batch) return;
-  const int tile = kx % ntile, m0 = (tile / nt) * 128, n0 = (tile % nt) * 128;
+  const int tile = kx % ntile, m0 = (tile / nt) * MT, n0 = (tile % nt) * NTT;
   const uint32_t bytes = (uint32_t)p.batch * N * N * 2;
   const auto ar = make_rsrc(p.A, bytes), br = make_rsrc(p.B, bytes);
   const int base = bt * N * N;
@@ -319,10 +328,10 @@ __global__ __launch_bounds__(256) void tm_gemm_kernel(TmGemmArgs p) {
 
   // row-major [128][32] tiles: 16-byte chunk kc of row r stored at kc ^ ((r >> 2) & 3)
   auto off32 = [](int r, int kc) { return r * 32 + ((kc ^ ((r >> 2) & 3)) << 3); };
-  u32x4 la[2], lb[2];
+  u32x4 la[LA], lb[LB];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < LA; ++i) {
       const int q = t + 256 * i;
       if constexpr (!TA) {
         const int row = q >> 2, kc = q & 3, k = k0 + 8 * kc;
@@ -331,6 +340,10 @@ __global__ __launch_bounds__(256) void tm_gemm_kernel(TmGemmArgs p) {
         const int row = q >> 4, mc = q & 15, k = k0 + row;
         la[i] = buf_ld16(ar, k < N ? (uint32_t)(base + k * N + m0 + 8 * mc) * 2 : bytes);
       }
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int q = t + 256 * i;
       if constexpr (!TB) {
         const int row = q >> 2, kc = q & 3, k = k0 + 8 * kc;
         lb[i] = buf_ld16(br, k < N ? (uint32_t)(base + (n0 + row) * N + k) * 2 : bytes);
@@ -342,49 +355,53 @@ __global__ __launch_bounds__(256) void tm_gemm_kernel(TmGemmArgs p) {
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < LA; ++i) {
       const int q = t + 256 * i;
       if constexpr (!TA) st_lds16(sA[buf], off32(q >> 2, q & 3), la[i]);
       else st_lds16(sA[buf], toff(q >> 4, q & 15), la[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int q = t + 256 * i;
       if constexpr (!TB) st_lds16(sB[buf], off32(q >> 2, q & 3), lb[i]);
       else st_lds16(sB[buf], toff(q >> 4, q & 15), lb[i]);
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[NBB][MB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NBB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < MB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   load(0);
   for (int k0 = 0, step = 0; k0 < N; k0 += TK, ++step) {
     const int buf = step & 1;
     stash(buf);
     if (k0 + TK < N) load(k0 + TK);
     lds_barrier();
-    u32x4 fa[4], fb[4];
+    u32x4 fa[NBB], fb[MB];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int n = wn * 64 + nb * 16;
+    for (int nb = 0; nb < NBB; ++nb) {
+      const int n = wn * (NTT / 2) + nb * 16;
       if constexpr (!TB) fa[nb] = ld_lds16(sB[buf], off32(n + c, g));
       else fa[nb] = tr8_swz(sB[buf], 8 * g, n, lane);
     }
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = wm * 64 + mb * 16;
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = wm * (MT / 2) + mb * 16;
       if constexpr (!TA) fb[mb] = ld_lds16(sA[buf], off32(m + c, g));
       else fb[mb] = tr8_swz(sA[buf], 8 * g, m, lane);
     }
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NBB; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma_k32(fa[nb], fb[mb], acc[nb][mb]);
+      for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma_k32(fa[nb], fb[mb], acc[nb][mb]);
   }
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb = 0; nb < NBB; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 64 + mb * 16 + c, n = n0 + wn * 64 + nb * 16 + 4 * g;
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + wm * (MT / 2) + mb * 16 + c, n = n0 + wn * (NTT / 2) + nb * 16 + 4 * g;
       if (m < N && n < N)
         *reinterpret_cast<u32x2*>(p.C + base + m * N + n) =
             u32x2{pack_bf16(acc[nb][mb][0], acc[nb][mb][1]), pack_bf16(acc[nb][mb][2], acc[nb][mb][3])};
@@ -925,13 +942,20 @@ hipError_t launch_pairs(const Args& a, int tile, K64 k64, K128 k128, hipStream_t
   return hipGetLastError();
 }
 
+template <bool TA, bool TB, int MT>
+hipError_t launch_gemm_t(const TmGemmArgs& a, hipStream_t st) {
+  const int ntm = (a.N + MT - 1) / MT, nt = ntm;
+  const int grid = (a.batch + 7) / 8 * 8 * ntm * nt;
+  hipLaunchKernelGGL((tm_gemm_kernel<TA, TB, MT>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 template <bool TA, bool TB>
 hipError_t launch_gemm(const TmGemmArgs& a, hipStream_t st) {
   if (a.batch == 0 || a.N == 0) return hipSuccess;
-  const int nt = (a.N + 127) / 128;
-  const int grid = (a.batch + 7) / 8 * 8 * nt * nt;
-  hipLaunchKernelGGL((tm_gemm_kernel<TA, TB>), dim3(grid), dim3(256), 0, st, a);
-  return hipGetLastError();
+  if constexpr (!TA && !TB) {
+    if (a.N % 192 == 0) return launch_gemm_t<TA, TB, 192>(a, st);
+  }
+  return launch_gemm_t<TA, TB, 128>(a, st);
 }
 
 }  // namespace
