@@ -105,17 +105,18 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
   const BwdQPlan pl = a.p;
 
   // XCD-aware order: blocks are dispatched round-robin over 8 XCDs; the query tiles of one
-  // (example, group, key range, head) unit run on one XCD at the same pace, so each slice's
-  // K and V rows are fetched into its L2 once.
-  const int nunit = a.B * pl.n_groups * pl.n_ranges * H;
+  // (example, group, head) unit run on one XCD at the same pace, its key ranges interleaved
+  // (range fastest), so each slice's K and V rows and each query tile's Q and dO rows are
+  // fetched into that XCD's L2 once.
+  const int nunit = a.B * pl.n_groups * H;
   const int xcd = blockIdx.x % 8, kx = blockIdx.x / 8;
-  const int unit = (kx / pl.n_qt) * 8 + xcd;
+  const int r = kx % pl.n_ranges;
+  const int unit = (kx / (pl.n_ranges * pl.n_qt)) * 8 + xcd;
   if (unit >= nunit) return;
-  const int qt = kx % pl.n_qt;
+  const int qt = (kx / pl.n_ranges) % pl.n_qt;
   const int h = unit % H;
-  const int r = (unit / H) % pl.n_ranges;
-  const int l = (unit / (H * pl.n_ranges)) % pl.n_groups;
-  const int b = unit / (H * pl.n_ranges * pl.n_groups);
+  const int l = (unit / H) % pl.n_groups;
+  const int b = unit / (H * pl.n_groups);
 
   const int q0 = qt * TQ;
   const int kw0 = r * pl.kr + w * KWP;           // first key of this wave
@@ -348,8 +349,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwdq_kernel(BwdQArgs a) {
 
 template <int D, bool MASK, int NW, int NP>
 static hipError_t launch_bwdq_t(const BwdQArgs& a, hipStream_t s) {
-  const int64_t nunit = (int64_t)a.B * a.H * a.p.n_ranges * a.p.n_groups;
-  const int64_t nblk = 8 * ((nunit + 7) / 8) * a.p.n_qt;
+  const int64_t nunit = (int64_t)a.B * a.H * a.p.n_groups;
+  const int64_t nblk = 8 * ((nunit + 7) / 8) * a.p.n_qt * a.p.n_ranges;
   hipLaunchKernelGGL((bwdq_kernel<D, MASK, NW, NP>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
