@@ -299,9 +299,9 @@ __global__ __launch_bounds__(NT) void tm_in_bwd_kernel(TmInArgs a) {
 // and channel).  TA: A stored [k][m] (else [m][k]); TB: B stored [k][n] (else [n][k]).  The MFMA
 // forms C^T = opB^T opA^T so that a lane's four results are four consecutive n of one m.
 // 256 threads, MT x MT tile, waves 2 x 2 of MT/2 x MT/2, k step 32, operand tiles double-buffered.
-// MT = 192 when both operands are row-major and 192 divides n (4 x 4 tiles per matrix at n = 768:
-// with two workgroups per CU the 2048 tiles of 128 channels are exactly 4 rounds of the 256 CUs,
-// where 128 x 128 tiles left the last of 4.5 rounds half empty); 128 otherwise.
+// MT = 192 when 192 divides n (4 x 4 tiles per matrix at n = 768: with two workgroups per CU the
+// 2048 tiles of 128 channels are exactly 4 rounds of the 256 CUs, where 128 x 128 tiles left the
+// last of 4.5 rounds half empty); 128 otherwise.
 template <bool TA, bool TB, int MT>
 __global__ __launch_bounds__(256) void tm_gemm_kernel(TmGemmArgs p) {
   constexpr int TK = 32;
@@ -310,7 +310,8 @@ __global__ __launch_bounds__(256) void tm_gemm_kernel(TmGemmArgs p) {
   constexpr int NTT = MT;              // n rows of the tile (the B tile)
   constexpr int NBB = NTT / 32;        // 16-column blocks of a wave in n
   constexpr int LB = NTT / 64;
-  static_assert(MT == 128 || (MT == 192 && !TA && !TB), "192-row tiles only for row-major A and B");
+  static_assert(MT == 128 || MT == 192, "tiles of 128 or 192");
+  constexpr int CPR = MT / 8;          // 16-byte chunks per row of a transposed ([k][m]) tile
   __shared__ __align__(16) uint16_t sA[2][MT * TK];
   __shared__ __align__(16) uint16_t sB[2][NTT * TK];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
@@ -328,6 +329,19 @@ __global__ __launch_bounds__(256) void tm_gemm_kernel(TmGemmArgs p) {
 
   // row-major [128][32] tiles: 16-byte chunk kc of row r stored at kc ^ ((r >> 2) & 3)
   auto off32 = [](int r, int kc) { return r * 32 + ((kc ^ ((r >> 2) & 3)) << 3); };
+  // transposed tiles [32 k][MT]: 128-wide rows use the pair-tile swizzle (toff); 192-wide rows
+  // XOR the chunk (within its aligned group of 8) with 2 (row bit 1) and 4 (row bit 3), which
+  // keeps the transposing reads of rows 8g + 0..3 (+4) and the row-major stores conflict-free
+  auto offT = [](int r, int j) {
+    if constexpr (MT == 128) return toff(r, j);
+    else return r * MT + ((j ^ ((((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2))) << 3);
+  };
+  auto trT = [&](const uint16_t* tile, int row0, int col0) {
+    const int kk = (lane & 15) >> 2, a4 = lane & 3;
+    const int col = col0 + 4 * a4, j = col >> 3, half = (col >> 2) & 1;
+    const int r0 = row0 + kk, r1 = r0 + 4;
+    return ds_read_tr8_at(tile, offT(r0, j) + 4 * half, offT(r1, j) + 4 * half);
+  };
   u32x4 la[LA], lb[LB];
   auto load = [&](int k0) {
 #pragma unroll
@@ -337,7 +351,7 @@ __global__ __launch_bounds__(256) void tm_gemm_kernel(TmGemmArgs p) {
         const int row = q >> 2, kc = q & 3, k = k0 + 8 * kc;
         la[i] = buf_ld16(ar, k < N ? (uint32_t)(base + (m0 + row) * N + k) * 2 : bytes);
       } else {
-        const int row = q >> 4, mc = q & 15, k = k0 + row;
+        const int row = q / CPR, mc = q % CPR, k = k0 + row;
         la[i] = buf_ld16(ar, k < N ? (uint32_t)(base + k * N + m0 + 8 * mc) * 2 : bytes);
       }
     }
@@ -348,7 +362,7 @@ __global__ __launch_bounds__(256) void tm_gemm_kernel(TmGemmArgs p) {
         const int row = q >> 2, kc = q & 3, k = k0 + 8 * kc;
         lb[i] = buf_ld16(br, k < N ? (uint32_t)(base + (n0 + row) * N + k) * 2 : bytes);
       } else {
-        const int row = q >> 4, nc = q & 15, k = k0 + row;
+        const int row = q / CPR, nc = q % CPR, k = k0 + row;
         lb[i] = buf_ld16(br, k < N ? (uint32_t)(base + k * N + n0 + 8 * nc) * 2 : bytes);
       }
     }
@@ -358,13 +372,13 @@ __global__ __launch_bounds__(256) void tm_gemm_kernel(TmGemmArgs p) {
     for (int i = 0; i < LA; ++i) {
       const int q = t + 256 * i;
       if constexpr (!TA) st_lds16(sA[buf], off32(q >> 2, q & 3), la[i]);
-      else st_lds16(sA[buf], toff(q >> 4, q & 15), la[i]);
+      else st_lds16(sA[buf], offT(q / CPR, q % CPR), la[i]);
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       const int q = t + 256 * i;
       if constexpr (!TB) st_lds16(sB[buf], off32(q >> 2, q & 3), lb[i]);
-      else st_lds16(sB[buf], toff(q >> 4, q & 15), lb[i]);
+      else st_lds16(sB[buf], offT(q / CPR, q % CPR), lb[i]);
     }
   };
 
@@ -384,13 +398,13 @@ __global__ __launch_bounds__(256) void tm_gemm_kernel(TmGemmArgs p) {
     for (int nb = 0; nb < NBB; ++nb) {
       const int n = wn * (NTT / 2) + nb * 16;
       if constexpr (!TB) fa[nb] = ld_lds16(sB[buf], off32(n + c, g));
-      else fa[nb] = tr8_swz(sB[buf], 8 * g, n, lane);
+      else fa[nb] = trT(sB[buf], 8 * g, n);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int m = wm * (MT / 2) + mb * 16;
       if constexpr (!TA) fb[mb] = ld_lds16(sA[buf], off32(m + c, g));
-      else fb[mb] = tr8_swz(sA[buf], 8 * g, m, lane);
+      else fb[mb] = trT(sA[buf], 8 * g, m);
     }
 #pragma unroll
     for (int nb = 0; nb < NBB; ++nb)
@@ -952,9 +966,7 @@ hipError_t launch_gemm_t(const TmGemmArgs& a, hipStream_t st) {
 template <bool TA, bool TB>
 hipError_t launch_gemm(const TmGemmArgs& a, hipStream_t st) {
   if (a.batch == 0 || a.N == 0) return hipSuccess;
-  if constexpr (!TA && !TB) {
-    if (a.N % 192 == 0) return launch_gemm_t<TA, TB, 192>(a, st);
-  }
+  if (a.N % 192 == 0) return launch_gemm_t<TA, TB, 192>(a, st);
   return launch_gemm_t<TA, TB, 128>(a, st);
 }
 
