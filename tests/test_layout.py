@@ -61,3 +61,31 @@ def test_access_shapes_conflict_free():
             assert _free16([_byte(swz, base + r, 2 * h + dc) for r in range(16) for dc in range(2)])
         for r0 in range(base, base + 16, 2):
             assert _free16([_byte(swz, r, j) for r in (r0, r0 + 1) for j in range(16)])
+
+
+def _swz192():
+    src = open(os.path.join(ROOT, "triangular_attention_amd", "csrc", "trimul.hip")).read()
+    m = re.search(r"else return r \* MT \+ \(\(j \^ (.*?)\) << 3\);", src)
+    assert m, "192-wide swizzle not found"
+    expr = m.group(1)
+    assert re.fullmatch(r"[r0-9&|^<>()\s]+", expr), expr
+    return lambda r: eval(expr, {}, {"r": r})
+
+
+def test_contraction_192_wide_tiles_conflict_free():
+    """The [32 k][192] operand tiles of the per-channel products: chunks stay in their row, the
+    transposing reads (rows 8g + 0..3 and + 4, two adjacent chunks, both halves) and the
+    row-major stores (32 consecutive 16-byte chunks) are conflict-free."""
+    f = _swz192()
+
+    def addr(r, j, half=0):
+        return r * 384 + 16 * (j ^ f(r)) + 8 * half
+
+    assert all(0 <= (j ^ f(r)) < 24 and (j ^ f(r)) // 8 == j // 8 for r in range(32) for j in range(24))
+    for base in (0, 16):
+        for extra in (0, 4):
+            rows = [base + 8 * g + kk + extra for g in (0, 1) for kk in range(4)]
+            for j0 in range(0, 24, 2):
+                assert _free8([addr(r, j, h) for r in rows for j in (j0, j0 + 1) for h in (0, 1)])
+    for q0 in range(0, 32 * 24, 32):
+        assert _free16([addr(q // 24, q % 24) for q in range(q0, q0 + 32)])
