@@ -673,7 +673,7 @@ __global__ __launch_bounds__(256) void blk_reduce_kernel(BlkReduceArgs a) {
 hipError_t launch_blk_ln_proj(const BlkLnProjArgs& a, hipStream_t st)
     TRI_BLK_LAUNCH(ln_proj_kernel, a, kBlkTileFwd, kBlkMaxWG)
 hipError_t launch_blk_gate_out(const BlkGateOutArgs& a, hipStream_t st)
-    TRI_BLK_LAUNCH(gate_out_kernel, a, kBlkTileFwd, kBlkMaxWG)
+    TRI_BLK_LAUNCH(gate_out_kernel, a, kBlkTileFwd, 2 * kBlkMaxWG)   // 88 VGPRs, 64 KB LDS: two per CU
 hipError_t launch_blk_gate_out_bwd(const BlkGateOutArgs& a, hipStream_t st)
     TRI_BLK_LAUNCH(gate_out_bwd_kernel, a, kBlkTileOutBwd, kBlkMaxWG)
 hipError_t launch_blk_proj_dz(const BlkProjBwdArgs& a, hipStream_t st)
